@@ -1,0 +1,233 @@
+"""Benchmark of the slot-indexed Gated DeltaNet state path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Prints ONE JSON line.  `value` is the decode step's algorithmic HBM traffic
+per second (GB/s) on the decode workload: 256 rows x 1 token, 32 v-heads /
+16 k-heads, 128x128 fp32 state per head, 8192 bf16 conv channels with 4
+taps, 1024-slot pool with pages padded to 4 KiB, 90 % of the rows warm.
+Alongside: varlen prefill tokens/s (8 sequences of U{512..4096} tokens, 16
+heads) and the cross-layer restore GB/s (48 GDN layers of a 64-layer stack,
+64 ops, a quarter of them misses).  Inputs are synthetic and resident in HBM
+before timing; timing uses HIP events on the stream the kernels run on.
+The CPU baseline is the oracle timed on this host on the same decode batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+METRIC = "GDN decode state GB/s (% HBM peak) + prefill tokens/s, 32 heads x 128x128 fp32"
+
+
+def decode_bytes(inp) -> int:
+    """Algorithmic bytes of one decode step: state read for warm rows and
+    written for all rows, window read (warm) and written, x, alpha, beta,
+    output, conv weights, state index and flag."""
+    g = inp.geom
+    B = inp.num_seqs
+    n_w = int(inp.has_initial_state.sum())
+    tile = g.Hv * g.dk * g.dv * 4
+    win = (g.W - 1) * g.C * 2
+    return (n_w * tile + B * tile + n_w * win + B * win + B * g.C * 2 + B * g.Hv * 8
+            + B * g.Hv * g.dv * 2 + g.C * g.W * 2 + 5 * B)
+
+
+def prefill_bytes(inp) -> int:
+    g = inp.geom
+    T = inp.total_tokens
+    n = inp.num_seqs
+    n_w = int(inp.has_initial_state.sum())
+    tile = g.Hv * g.dk * g.dv * 4
+    win = (g.W - 1) * g.C * 2
+    return (T * g.C * 2 + T * g.Hv * 8 + T * g.Hv * g.dv * 2 + (n_w + n) * (tile + win)
+            + g.C * g.W * 2 + 9 * n)
+
+
+def timed(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per call
+
+
+def dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+
+def bench_decode(steps, warmup):
+    import torch
+    import hybrid_linear_attention_slot_amd as gdn
+    import workloads as wl
+
+    inp, pages = wl.decode_workload(seed=0)
+    g = inp.geom
+    pool = torch.zeros((g.num_slots, g.page_stride), dtype=torch.uint8, device="cuda")
+    idx = torch.from_numpy(inp.state_indices.astype(np.int64)).cuda()
+    pool[idx] = torch.from_numpy(pages).cuda()
+    h = gdn.gdn_pool_create([pool], g.num_slots, g.page_stride, g.conv_off, g.ssm_off, g.C,
+                            g.W, g.Hk, g.Hv, g.dk, g.dv)
+    out = torch.empty((inp.num_seqs, g.Hv, g.dv), dtype=torch.int16, device="cuda")
+    args = gdn.make_step_args(dev(inp.x), dev(inp.conv_w), None, dev(inp.alpha), dev(inp.beta),
+                              dev(inp.state_indices), dev(inp.has_initial_state), out, 1.0, 1e-6)
+    stream = torch.cuda.current_stream()
+    ms = timed(lambda: gdn.gdn_decode_step(h, 0, inp.num_seqs, args, stream), steps, warmup,
+               stream)
+    return inp, ms, decode_bytes(inp)
+
+
+def bench_prefill(steps, warmup):
+    import torch
+    import hybrid_linear_attention_slot_amd as gdn
+    import workloads as wl
+
+    inp, img = wl.prefill_workload(seed=0)
+    g = inp.geom
+    pool = dev(img)
+    h = gdn.gdn_pool_create([pool], g.num_slots, g.page_stride, g.conv_off, g.ssm_off, g.C,
+                            g.W, g.Hk, g.Hv, g.dk, g.dv)
+    out = torch.empty((inp.total_tokens, g.Hv, g.dv), dtype=torch.int16, device="cuda")
+    args = gdn.make_step_args(dev(inp.x), dev(inp.conv_w), None, dev(inp.alpha), dev(inp.beta),
+                              dev(inp.state_indices), dev(inp.has_initial_state), out, 1.0, 1e-6)
+    cu = dev(inp.cu_seqlens)
+    stream = torch.cuda.current_stream()
+    ms = timed(lambda: gdn.gdn_prefill_varlen(h, 0, inp.num_seqs, cu, inp.max_seqlen,
+                                              inp.total_tokens, args, stream),
+               max(2, steps // 5), max(1, warmup // 5), stream)
+    return inp, ms
+
+
+def bench_restore(steps, warmup):
+    import torch
+    import hybrid_linear_attention_slot_amd as gdn
+    import workloads as wl
+
+    g, linear, ops = wl.restore_workload(seed=0)
+    bufs = [torch.empty((g.num_slots, g.page_stride), dtype=torch.uint8, device="cuda")
+            if lin else None for lin in linear]
+    h = gdn.gdn_pool_create(bufs, g.num_slots, g.page_stride, g.conv_off, g.ssm_off, g.C, g.W,
+                            g.Hk, g.Hv, g.dk, g.dv)
+    hs = torch.ones(len(ops), dtype=torch.uint8, device="cuda")
+    op_list = ops.tolist()
+    stream = torch.cuda.current_stream()
+    ms = timed(lambda: gdn.gdn_restore_slots(h, op_list, hs, stream), max(2, steps // 5),
+               max(1, warmup // 5), stream)
+    hits = int((ops[:, 1] >= 0).sum())
+    nbytes = 2 * hits * int(linear.sum()) * (g.ssm_region_bytes + g.conv_region_bytes)
+    del bufs
+    torch.cuda.empty_cache()
+    return ms, nbytes, hits, int(linear.sum())
+
+
+def cpu_baseline(inp_decode, min_seconds=10.0):
+    """The oracle on this host, on the decode batch, repeated for >= min_seconds."""
+    import dataclasses
+
+    import oracle
+    import workloads as wl
+
+    threads = min(os.cpu_count() or 1, 16)
+    oracle.set_threads(threads)
+    _, pages = wl.decode_workload(seed=0)
+    sub = dataclasses.replace(inp_decode.geom, num_slots=inp_decode.num_seqs)
+    loc = np.arange(inp_decode.num_seqs, dtype=np.int32)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        work = pages.copy()
+        oracle.gdn_layer(work, sub, inp_decode.cu_seqlens, loc, inp_decode.has_initial_state,
+                         inp_decode.x, inp_decode.conv_w, inp_decode.conv_b, inp_decode.alpha,
+                         inp_decode.beta)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(decode_bytes(inp_decode) * reps / dt / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.get_threads(), "kind": "oracle",
+            "sample": f"the full decode batch (256 rows x 32 heads) x {reps} repetitions, "
+                      f"{dt:.1f} s, fp64 C oracle with OpenMP over rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-restore", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: the slot-state path has no cross-GPU step "
+              "(each data-parallel rank owns its own pool); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import hybrid_linear_attention_slot_amd as gdn
+    gdn.lib()
+
+    inp, ms, nbytes = bench_decode(a.steps, a.warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    pinp, pms = bench_prefill(a.steps, a.warmup)
+    prefill = {"tokens_per_s": round(pinp.total_tokens / (pms * 1e-3), 1),
+               "ms_per_call": round(pms, 4), "tokens": pinp.total_tokens,
+               "max_seqlen": pinp.max_seqlen,
+               "us_per_token_critical_path": round(pms * 1e3 / pinp.max_seqlen, 4),
+               "gb_per_s": round(prefill_bytes(pinp) / (pms * 1e-3) / 1e9, 2),
+               "workload": "8 seqs, lengths U{512..4096}, 16 v-heads/8 k-heads, 128x128 fp32, "
+                           "4 warm + 4 cold"}
+    restore = None
+    if not a.no_restore:
+        rms, rbytes, hits, nlin = bench_restore(a.steps, a.warmup)
+        restore = {"gb_per_s": round(rbytes / (rms * 1e-3) / 1e9, 2), "ms_per_call": round(rms, 4),
+                   "bytes": rbytes, "hits": hits, "gdn_layers": nlin,
+                   "frac_of_hbm_peak": round(rbytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode step: 256 rows x 1 token, 32 v-heads / 16 k-heads, "
+                               "128x128 fp32 state, conv 8192 bf16 x 4 taps, 1024-slot pool, "
+                               "4 KiB-padded pages, 90% warm",
+                   "rows": inp.num_seqs, "warm_rows": int(inp.has_initial_state.sum()),
+                   "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "prefill": prefill,
+        "restore": restore,
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,216 @@
+"""Python binding of libgdn (the slot-indexed Gated DeltaNet state library).
+
+Argument marshalling only: every function forwards to the C-ABI entry point
+of the same name (include/gdn.h), which validates and enqueues gfx950 kernels
+on the given stream.  Device buffers may be given as torch tensors (their
+data_ptr() is used) or as integer addresses.  The library must have been
+built (`python -m hybrid_linear_attention_slot_amd.build`); there is no
+fallback: loading fails loudly when libgdn.so is missing.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+GDN_OK = 0
+GDN_WARN_COLD_FALLBACK = 1
+GDN_EINVAL = -1
+GDN_ERANGE = -2
+GDN_EOVERLAP = -3
+GDN_EALIGN = -4
+GDN_EUNSUPPORTED = -5
+GDN_EHIP = -6
+
+ERROR_NAMES = {GDN_EINVAL: "GDN_EINVAL", GDN_ERANGE: "GDN_ERANGE", GDN_EOVERLAP: "GDN_EOVERLAP",
+               GDN_EALIGN: "GDN_EALIGN", GDN_EUNSUPPORTED: "GDN_EUNSUPPORTED",
+               GDN_EHIP: "GDN_EHIP"}
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+class gdn_pool_desc(C.Structure):
+    _fields_ = [("num_layers", C.c_int32),
+                ("layer_base", C.POINTER(C.c_void_p)),
+                ("num_slots", C.c_int64),
+                ("page_stride_bytes", C.c_int64),
+                ("conv_offset_bytes", C.c_int64),
+                ("ssm_offset_bytes", C.c_int64),
+                ("conv_channels", C.c_int32),
+                ("conv_width", C.c_int32),
+                ("num_k_heads", C.c_int32),
+                ("num_v_heads", C.c_int32),
+                ("head_k_dim", C.c_int32),
+                ("head_v_dim", C.c_int32)]
+
+
+class gdn_restore_op(C.Structure):
+    _fields_ = [("dst_slot", C.c_int32), ("src_slot", C.c_int32), ("requested", C.c_int32)]
+
+
+class gdn_step_args(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("conv_w", C.c_void_p), ("conv_b", C.c_void_p),
+                ("alpha", C.c_void_p), ("beta", C.c_void_p), ("state_indices", C.c_void_p),
+                ("has_initial_state", C.c_void_p), ("out", C.c_void_p),
+                ("scale", C.c_float), ("l2_eps", C.c_float)]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded libgdn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m hybrid_linear_attention_slot_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        p, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+        L.gdn_pool_create.argtypes = [C.POINTER(gdn_pool_desc), C.POINTER(C.c_void_p)]
+        L.gdn_pool_create.restype = C.c_int
+        L.gdn_pool_destroy.argtypes = [p]
+        L.gdn_pool_destroy.restype = None
+        L.gdn_pool_region_bytes.argtypes = [p, C.POINTER(i64), C.POINTER(i64)]
+        L.gdn_pool_region_bytes.restype = C.c_int
+        L.gdn_pool_describe.argtypes = [p, C.c_char_p, C.c_size_t]
+        L.gdn_pool_describe.restype = C.c_int
+        L.gdn_restore_slots.argtypes = [p, C.POINTER(gdn_restore_op), i32, p, p]
+        L.gdn_restore_slots.restype = C.c_int
+        L.gdn_gather_states.argtypes = [p, i32, p, i32, p, p, p]
+        L.gdn_gather_states.restype = C.c_int
+        L.gdn_scatter_states.argtypes = [p, i32, p, i32, p, p, p]
+        L.gdn_scatter_states.restype = C.c_int
+        L.gdn_decode_step.argtypes = [p, i32, i32, C.POINTER(gdn_step_args), p]
+        L.gdn_decode_step.restype = C.c_int
+        L.gdn_prefill_varlen.argtypes = [p, i32, i32, p, i32, i64, C.POINTER(gdn_step_args), p]
+        L.gdn_prefill_varlen.restype = C.c_int
+        L.gdn_last_error.argtypes = []
+        L.gdn_last_error.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _addr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise GdnError(rc, gdn_last_error())
+    return rc
+
+
+def gdn_last_error() -> str:
+    return lib().gdn_last_error().decode()
+
+
+class Pool:
+    """Owner of a gdn_pool handle (host metadata only)."""
+
+    def __init__(self, handle: int, desc: gdn_pool_desc, bases):
+        self.handle = handle
+        self.desc = desc
+        self._bases = bases  # keeps the ctypes array alive while the pool lives
+
+    def close(self):
+        if self.handle:
+            lib().gdn_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gdn_pool_create(layer_base: Sequence, num_slots: int, page_stride_bytes: int,
+                    conv_offset_bytes: int, ssm_offset_bytes: int, conv_channels: int,
+                    conv_width: int, num_k_heads: int, num_v_heads: int, head_k_dim: int,
+                    head_v_dim: int) -> Pool:
+    """layer_base: per layer a device buffer (tensor or address) of num_slots
+    pages, or None for an attention-only layer."""
+    bases = (C.c_void_p * len(layer_base))(*[_addr(b) for b in layer_base])
+    d = gdn_pool_desc(len(layer_base), C.cast(bases, C.POINTER(C.c_void_p)), num_slots,
+                      page_stride_bytes, conv_offset_bytes, ssm_offset_bytes, conv_channels,
+                      conv_width, num_k_heads, num_v_heads, head_k_dim, head_v_dim)
+    h = C.c_void_p()
+    _check(lib().gdn_pool_create(C.byref(d), C.byref(h)))
+    return Pool(h.value, d, bases)
+
+
+def gdn_pool_destroy(pool: Pool) -> None:
+    pool.close()
+
+
+def gdn_pool_region_bytes(pool: Pool):
+    s, c = C.c_int64(), C.c_int64()
+    _check(lib().gdn_pool_region_bytes(pool.handle, C.byref(s), C.byref(c)))
+    return s.value, c.value
+
+
+def gdn_pool_describe(pool: Pool) -> str:
+    n = _check(lib().gdn_pool_describe(pool.handle, None, 0))
+    buf = C.create_string_buffer(n + 1)
+    _check(lib().gdn_pool_describe(pool.handle, buf, n + 1))
+    return buf.value.decode()
+
+
+def gdn_restore_slots(pool: Pool, ops, has_initial_state, stream=None) -> int:
+    """ops: sequence of (dst_slot, src_slot, requested) for batch rows 0..n-1.
+    Returns GDN_OK or GDN_WARN_COLD_FALLBACK."""
+    ops = [tuple(int(v) for v in op) for op in ops]
+    arr = (gdn_restore_op * max(1, len(ops)))(*[gdn_restore_op(*op) for op in ops])
+    return _check(lib().gdn_restore_slots(pool.handle, arr, len(ops), _addr(has_initial_state),
+                                          _stream(stream)))
+
+
+def gdn_gather_states(pool: Pool, layer: int, idx, n: int, ssm_dense, conv_dense,
+                      stream=None) -> int:
+    return _check(lib().gdn_gather_states(pool.handle, layer, _addr(idx), n, _addr(ssm_dense),
+                                          _addr(conv_dense), _stream(stream)))
+
+
+def gdn_scatter_states(pool: Pool, layer: int, idx, n: int, ssm_dense, conv_dense,
+                       stream=None) -> int:
+    return _check(lib().gdn_scatter_states(pool.handle, layer, _addr(idx), n, _addr(ssm_dense),
+                                           _addr(conv_dense), _stream(stream)))
+
+
+def make_step_args(x, conv_w, conv_b, alpha, beta, state_indices, has_initial_state, out,
+                   scale=1.0, l2_eps=1e-6) -> gdn_step_args:
+    return gdn_step_args(_addr(x), _addr(conv_w), _addr(conv_b), _addr(alpha), _addr(beta),
+                         _addr(state_indices), _addr(has_initial_state), _addr(out),
+                         float(scale), float(l2_eps))
+
+
+def gdn_decode_step(pool: Pool, layer: int, rows: int, args: gdn_step_args, stream=None) -> int:
+    return _check(lib().gdn_decode_step(pool.handle, layer, rows, C.byref(args),
+                                        _stream(stream)))
+
+
+def gdn_prefill_varlen(pool: Pool, layer: int, num_seqs: int, cu_seqlens, max_seqlen: int,
+                       total_tokens: int, args: gdn_step_args, stream=None) -> int:
+    return _check(lib().gdn_prefill_varlen(pool.handle, layer, num_seqs, _addr(cu_seqlens),
+                                           max_seqlen, total_tokens, C.byref(args),
+                                           _stream(stream)))

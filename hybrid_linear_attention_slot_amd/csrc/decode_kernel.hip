@@ -1,0 +1,361 @@
+// Fused decode step of a Gated DeltaNet layer over a page-strided slot pool
+// (gfx950).
+//
+// Per batch row: gather the row's conv window and recurrent state from its
+// slot ("非连续 KV Cache" §5: indexed access into the strided pool; zero
+// state when has_initial_state is 0, "Linear-State Prefix Cache 内部机制"
+// §4.1), run the depthwise causal conv update with SiLU ("非连续 KV Cache"
+// §6, the decode-time conv update), L2-normalise q and k, apply the gated
+// delta rule ("Kapitsa 源码拆解 05", section on what Gated DeltaNet keeps):
+//     S <- a S;  u = S k;  S <- S + b (v - u) k^T;  o = S q
+// and write window and state back into the same page ("Linear-State Prefix
+// Cache 内部机制" §0: the slot is overwritten in place every step).
+//
+// Design (HBM-bound; MFMA is of no use for rank-1 updates and mat-vecs):
+//   - one workgroup per (row, k-head g).  It owns the q and k conv channels
+//     of g and the v channels of the Hv/Hk v-heads that read g, so no two
+//     workgroups touch the same window channels, and q/k are computed once.
+//   - each v-head's dk x dv fp32 state tile is streamed once from HBM into
+//     registers and once back.  The tile is stored key-major ([dk][dv], value
+//     index contiguous).  A lane holds four consecutive value columns (one
+//     float4) for JPL keys; the LPC lanes that share a float4 column split
+//     the keys between them.  With dk = dv = 128: 4 waves, 8 columns of 16 B
+//     per key row per load instruction (8 full 128-byte lines), 16 float4 per
+//     lane.
+//   - S k and S q are lane-partial dot products over the lane's keys followed
+//     by a DPP sum over the LPC lanes; o is formed without a second pass over
+//     S:  o = a (S_old q) + d (k.q)  with  d = b (v - a S_old k).
+//   - the state loads of the first head are issued before the conv so that
+//     the conv and the norms overlap them.
+#include "device_utils.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+template <int DK, int DV>
+struct DecodeShape {
+    static constexpr int NCW = (DV / 4) < 8 ? (DV / 4) : 8; // float4 columns per wave
+    static constexpr int LPC = 64 / NCW;                    // lanes splitting one column's keys
+    static constexpr int JPL = DK / LPC;                    // keys per lane
+    static constexpr int NW = DV / (4 * NCW);               // waves per head tile
+    static constexpr int NT = 64 * NW;
+    static_assert(JPL >= 1 && NW >= 1 && DK % LPC == 0, "unsupported head dims");
+};
+
+struct DecodeParams {
+    uint8_t* layer;
+    int64_t page_stride;
+    int64_t ssm_off;
+    int64_t conv_off;
+    int32_t num_slots;
+    int32_t C;
+    int32_t Hk;
+    int32_t Hv;
+    const uint16_t* x;
+    const uint16_t* conv_w;
+    const uint16_t* conv_b;
+    const float* alpha;
+    const float* beta;
+    const int32_t* state_indices;
+    const uint8_t* hs;
+    uint16_t* out;
+    float scale;
+    float eps;
+};
+
+template <int DK, int DV, int JPL, int LPC>
+__device__ __forceinline__ void load_tile(float4 (&s)[JPL], const float* tile, int jl, int i0)
+{
+#pragma unroll
+    for (int m = 0; m < JPL; ++m)
+        s[m] = *reinterpret_cast<const float4*>(tile + (jl + LPC * m) * DV + i0);
+}
+
+// Conv inputs of one pair of adjacent channels (c, c+1), kept as the raw
+// words that were loaded: nothing is unpacked until every load of the
+// workgroup's first phase has been issued.
+template <int W>
+struct ConvPairIn {
+    uint32_t x;          // current inputs, bf16 x2
+    uint32_t win[W - 1]; // window rows, oldest first, bf16 x2
+    uint32_t w[W];       // taps of c then taps of c+1: 2W bf16
+    uint32_t b;          // bias of c and c+1, bf16 x2 (0 without bias)
+};
+
+__device__ __forceinline__ float lo_bf16(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// bf16 number k of the packed sequence in `w`
+template <int K, int W>
+__device__ __forceinline__ float tap(const uint32_t (&w)[W])
+{
+    return (K & 1) ? hi_bf16(w[K >> 1]) : lo_bf16(w[K >> 1]);
+}
+
+template <int W>
+__device__ __forceinline__ void load_conv_pair(ConvPairIn<W>& in, const DecodeParams& p, int row,
+                                               int c, const uint32_t* wp, bool warm)
+{
+    in.x = *reinterpret_cast<const uint32_t*>(p.x + int64_t(row) * p.C + c);
+#pragma unroll
+    for (int w = 0; w < W - 1; ++w)
+        in.win[w] = warm ? wp[w * (p.C / 2)] : 0u;
+    const uint32_t* wsrc = reinterpret_cast<const uint32_t*>(p.conv_w + int64_t(c) * W);
+#pragma unroll
+    for (int k = 0; k < W; ++k)
+        in.w[k] = wsrc[k];
+    in.b = p.conv_b ? *reinterpret_cast<const uint32_t*>(p.conv_b + c) : 0u;
+}
+
+template <int W, int T = 0>
+__device__ __forceinline__ void conv_taps(const ConvPairIn<W>& in, float& acc0, float& acc1)
+{
+    if constexpr (T < W - 1) {
+        acc0 += tap<T, W>(in.w) * lo_bf16(in.win[T]);
+        acc1 += tap<W + T, W>(in.w) * hi_bf16(in.win[T]);
+        conv_taps<W, T + 1>(in, acc0, acc1);
+    }
+}
+
+// SiLU(conv) of both channels into LDS; the window is rewritten shifted by
+// one input with the current input appended.
+template <int W>
+__device__ __forceinline__ void finish_conv_pair(const ConvPairIn<W>& in, uint32_t* wp, int C,
+                                                 float* y)
+{
+    float acc0 = lo_bf16(in.b), acc1 = hi_bf16(in.b);
+    conv_taps<W>(in, acc0, acc1);
+    acc0 += tap<W - 1, W>(in.w) * lo_bf16(in.x);
+    acc1 += tap<2 * W - 1, W>(in.w) * hi_bf16(in.x);
+#pragma unroll
+    for (int w = 0; w + 1 < W - 1; ++w)
+        wp[w * (C / 2)] = in.win[w + 1];
+    wp[(W - 2) * (C / 2)] = in.x;
+    y[0] = silu(acc0);
+    y[1] = silu(acc1);
+}
+
+// One (row, k-head group).  WARM is a template parameter so that the cold
+// path (no state loads) and the warm path each get exact memory waits.
+template <int DK, int DV, int W, bool WARM>
+__device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, int row, int g,
+                                             uint8_t* page)
+{
+    using Sh = DecodeShape<DK, DV>;
+    constexpr int JPL = Sh::JPL, LPC = Sh::LPC;
+    const int G = p.Hv / p.Hk;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int jl = lane % LPC;
+    const int i0 = 4 * (wave * Sh::NCW + lane / LPC);
+    const int h0 = g * G;
+    uint16_t* out_row = p.out + (int64_t(row) * p.Hv + h0) * DV;
+    float* ssm = reinterpret_cast<float*>(page + p.ssm_off);
+    uint16_t* win = reinterpret_cast<uint16_t*>(page + p.conv_off);
+    const int C = p.C;
+
+    // workgroup channel pair -> global channel: q of g | k of g | v of the group
+    const int nvc = 2 * DK + G * DV;
+    auto chan = [&](int vc) -> int {
+        if (vc < DK)
+            return g * DK + vc;
+        if (vc < 2 * DK)
+            return p.Hk * DK + g * DK + (vc - DK);
+        return 2 * p.Hk * DK + h0 * DV + (vc - 2 * DK);
+    };
+
+    // 1. conv inputs of the first channel pair, then the first head's state
+    //    tile: loads complete in issue order, so the conv can start while the
+    //    tile is still in flight
+    ConvPairIn<W> cin;
+    const int vc0 = 2 * tid;
+    const int c0 = chan(vc0 < nvc ? vc0 : 0);
+    if (vc0 < nvc)
+        load_conv_pair<W>(cin, p, row, c0, reinterpret_cast<const uint32_t*>(win + c0), WARM);
+    float4 s[JPL];
+    if constexpr (WARM) {
+        load_tile<DK, DV, JPL, LPC>(s, ssm + int64_t(h0) * DK * DV, jl, i0);
+    } else {
+#pragma unroll
+        for (int m = 0; m < JPL; ++m)
+            s[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    // 2. conv + SiLU; groups with more channels than 2 per thread loop on
+    if (vc0 < nvc)
+        finish_conv_pair<W>(cin, reinterpret_cast<uint32_t*>(win + c0), C, ys + vc0);
+    for (int vc = vc0 + 2 * Sh::NT; vc < nvc; vc += 2 * Sh::NT) {
+        const int c = chan(vc);
+        ConvPairIn<W> in;
+        load_conv_pair<W>(in, p, row, c, reinterpret_cast<const uint32_t*>(win + c), WARM);
+        finish_conv_pair<W>(in, reinterpret_cast<uint32_t*>(win + c), C, ys + vc);
+    }
+    __syncthreads();
+
+    // 3. L2 norms and k.q; every wave reduces redundantly (no second barrier)
+    float sq = 0.f, sk = 0.f, qk = 0.f;
+    for (int j = lane; j < DK; j += 64) {
+        const float a = ys[j], b = ys[DK + j];
+        sq += a * a;
+        sk += b * b;
+        qk += a * b;
+    }
+    sq = group_sum<64>(sq);
+    sk = group_sum<64>(sk);
+    qk = group_sum<64>(qk);
+    const float rq = p.scale / sqrtf(sq + p.eps);
+    const float rk = 1.0f / sqrtf(sk + p.eps);
+    const float kq = qk * rq * rk;
+    float kh[JPL], qh[JPL];
+#pragma unroll
+    for (int m = 0; m < JPL; ++m) {
+        const int j = jl + LPC * m;
+        qh[m] = ys[j] * rq;
+        kh[m] = ys[DK + j] * rk;
+    }
+
+    // 4. gated delta rule, one v-head after another
+    for (int hh = 0; hh < G; ++hh) {
+        const int h = h0 + hh;
+        float* tile = ssm + int64_t(h) * DK * DV;
+        if constexpr (WARM) {
+            if (hh > 0)
+                load_tile<DK, DV, JPL, LPC>(s, tile, jl, i0);
+        }
+        float4 u = make_float4(0.f, 0.f, 0.f, 0.f), o = u;
+#pragma unroll
+        for (int m = 0; m < JPL; ++m) {
+            u.x += s[m].x * kh[m];
+            u.y += s[m].y * kh[m];
+            u.z += s[m].z * kh[m];
+            u.w += s[m].w * kh[m];
+            o.x += s[m].x * qh[m];
+            o.y += s[m].y * qh[m];
+            o.z += s[m].z * qh[m];
+            o.w += s[m].w * qh[m];
+        }
+        u.x = group_sum<LPC>(u.x);
+        u.y = group_sum<LPC>(u.y);
+        u.z = group_sum<LPC>(u.z);
+        u.w = group_sum<LPC>(u.w);
+        o.x = group_sum<LPC>(o.x);
+        o.y = group_sum<LPC>(o.y);
+        o.z = group_sum<LPC>(o.z);
+        o.w = group_sum<LPC>(o.w);
+        const float a = p.alpha[int64_t(row) * p.Hv + h];
+        const float b = p.beta[int64_t(row) * p.Hv + h];
+        const float* v = ys + 2 * DK + hh * DV + i0;
+        float4 d;
+        d.x = b * (v[0] - a * u.x);
+        d.y = b * (v[1] - a * u.y);
+        d.z = b * (v[2] - a * u.z);
+        d.w = b * (v[3] - a * u.w);
+#pragma unroll
+        for (int m = 0; m < JPL; ++m) {
+            float4 t;
+            t.x = fmaf(d.x, kh[m], a * s[m].x);
+            t.y = fmaf(d.y, kh[m], a * s[m].y);
+            t.z = fmaf(d.z, kh[m], a * s[m].z);
+            t.w = fmaf(d.w, kh[m], a * s[m].w);
+            *reinterpret_cast<float4*>(tile + (jl + LPC * m) * DV + i0) = t;
+        }
+        if (jl == 0) {
+            const float o0 = fmaf(d.x, kq, a * o.x);
+            const float o1 = fmaf(d.y, kq, a * o.y);
+            const float o2 = fmaf(d.z, kq, a * o.z);
+            const float o3 = fmaf(d.w, kq, a * o.w);
+            *reinterpret_cast<uint2*>(out_row + hh * DV + i0) = pack_bf16x4(o0, o1, o2, o3);
+        }
+    }
+}
+
+template <int DK, int DV, int W>
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(DecodeParams p)
+{
+    using Sh = DecodeShape<DK, DV>;
+    extern __shared__ float ys[]; // conv outputs: q (DK) | k (DK) | v (G*DV)
+    const int row = blockIdx.x / p.Hk;
+    const int g = blockIdx.x - row * p.Hk;
+    const int slot = p.state_indices[row];
+    if (slot < 0 || slot >= p.num_slots) { // padding row: zero output, no state I/O
+        const int G = p.Hv / p.Hk;
+        uint16_t* out_row = p.out + (int64_t(row) * p.Hv + g * G) * DV;
+        for (int e = threadIdx.x; e < G * DV; e += Sh::NT)
+            out_row[e] = 0;
+        return;
+    }
+    uint8_t* page = p.layer + int64_t(slot) * p.page_stride;
+    if (p.hs[row] != 0)
+        decode_group<DK, DV, W, true>(p, ys, row, g, page);
+    else
+        decode_group<DK, DV, W, false>(p, ys, row, g, page);
+}
+
+template <int DK, int DV, int W>
+int launch_decode_t(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn_step_args* a,
+                    hipStream_t stream)
+{
+    using Sh = DecodeShape<DK, DV>;
+    const gdn_pool_desc& d = pool->desc;
+    DecodeParams p;
+    p.layer = static_cast<uint8_t*>(pool->bases[layer]);
+    p.page_stride = d.page_stride_bytes;
+    p.ssm_off = d.ssm_offset_bytes;
+    p.conv_off = d.conv_offset_bytes;
+    p.num_slots = int32_t(d.num_slots);
+    p.C = d.conv_channels;
+    p.Hk = d.num_k_heads;
+    p.Hv = d.num_v_heads;
+    p.x = a->x;
+    p.conv_w = a->conv_w;
+    p.conv_b = a->conv_b;
+    p.alpha = a->alpha;
+    p.beta = a->beta;
+    p.state_indices = a->state_indices;
+    p.hs = a->has_initial_state;
+    p.out = a->out;
+    p.scale = a->scale;
+    p.eps = a->l2_eps;
+    const int G = d.num_v_heads / d.num_k_heads;
+    const size_t lds = sizeof(float) * size_t(2 * DK + G * DV);
+    const int64_t blocks = int64_t(rows) * d.num_k_heads;
+    if (blocks > INT32_MAX)
+        return fail(GDN_ERANGE, "decode grid too large");
+    hipLaunchKernelGGL((decode_kernel<DK, DV, W>), dim3(uint32_t(blocks)), dim3(Sh::NT), lds, stream,
+                       p);
+    return check_launch("decode");
+}
+
+template <int DK>
+int dispatch_w(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn_step_args* a,
+               hipStream_t stream)
+{
+    switch (pool->desc.conv_width) {
+    case 2: return launch_decode_t<DK, DK, 2>(pool, layer, rows, a, stream);
+    case 3: return launch_decode_t<DK, DK, 3>(pool, layer, rows, a, stream);
+    case 4: return launch_decode_t<DK, DK, 4>(pool, layer, rows, a, stream);
+    default: return fail(GDN_EUNSUPPORTED, "decode: conv width %d", pool->desc.conv_width);
+    }
+}
+
+} // namespace
+
+bool decode_supported(int dk, int dv, int W)
+{
+    return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128) && W >= 2 && W <= 4;
+}
+
+int launch_decode(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn_step_args* a,
+                  hipStream_t stream)
+{
+    switch (pool->desc.head_k_dim) {
+    case 16: return dispatch_w<16>(pool, layer, rows, a, stream);
+    case 32: return dispatch_w<32>(pool, layer, rows, a, stream);
+    case 64: return dispatch_w<64>(pool, layer, rows, a, stream);
+    case 128: return dispatch_w<128>(pool, layer, rows, a, stream);
+    default: return fail(GDN_EUNSUPPORTED, "decode: head dim %d", pool->desc.head_k_dim);
+    }
+}
+
+} // namespace gdn

@@ -1,0 +1,347 @@
+// C-ABI entry points of the GDN state library: pool descriptor, validation,
+// error reporting, and dispatch to the gfx950 kernels.  Everything here runs
+// on the host and never synchronises with the device.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+#include <unordered_set>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+int check_launch(const char* what)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(GDN_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return GDN_OK;
+}
+
+} // namespace gdn
+
+using gdn::fail;
+
+namespace {
+
+bool aligned16(int64_t v) { return (v & 15) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) intersect (empty ranges never do).
+bool overlaps(int64_t a, int64_t na, int64_t b, int64_t nb)
+{
+    if (na == 0 || nb == 0)
+        return false;
+    return a < b + nb && b < a + na;
+}
+
+int check_layer(const gdn_pool* pool, int32_t layer)
+{
+    if (layer < 0 || layer >= pool->desc.num_layers)
+        return fail(GDN_ERANGE, "layer %d outside [0, %d)", layer, pool->desc.num_layers);
+    if (pool->bases[layer] == nullptr)
+        return fail(GDN_ERANGE, "layer %d is attention-only (no state pool)", layer);
+    return GDN_OK;
+}
+
+int check_step_args(const gdn_pool* pool, int32_t layer, const gdn_step_args* a)
+{
+    int rc = check_layer(pool, layer);
+    if (rc != GDN_OK)
+        return rc;
+    if (a == nullptr)
+        return fail(GDN_EINVAL, "args is NULL");
+    if (!a->x || !a->conv_w || !a->alpha || !a->beta || !a->state_indices ||
+        !a->has_initial_state || !a->out)
+        return fail(GDN_EINVAL, "a required device pointer in args is NULL");
+    if (pool->desc.num_v_heads == 0)
+        return fail(GDN_EUNSUPPORTED, "conv-window-only pool has no recurrent state");
+    if (!(a->l2_eps >= 0.0f))
+        return fail(GDN_EINVAL, "l2_eps must be >= 0");
+    return GDN_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char* gdn_last_error(void) { return gdn::g_last_error.c_str(); }
+
+int gdn_pool_create(const gdn_pool_desc* d, gdn_pool** out)
+{
+    gdn::clear_error();
+    if (!d || !out)
+        return fail(GDN_EINVAL, "desc and out must not be NULL");
+    if (d->num_layers <= 0 || !d->layer_base)
+        return fail(GDN_EINVAL, "num_layers must be > 0 and layer_base non-NULL");
+    if (d->num_slots <= 0 || d->num_slots > INT32_MAX)
+        return fail(GDN_ERANGE, "num_slots %lld outside [1, 2^31)", (long long)d->num_slots);
+    if (d->conv_width < 2 || d->conv_width > 8)
+        return fail(GDN_EINVAL, "conv_width %d outside [2, 8]", d->conv_width);
+    if (d->conv_channels <= 0 || (d->conv_channels & 1))
+        return fail(GDN_EINVAL, "conv_channels %d must be positive and even", d->conv_channels);
+    if (d->num_v_heads < 0 || d->num_k_heads < 0 || d->head_k_dim < 0 || d->head_v_dim < 0)
+        return fail(GDN_EINVAL, "negative head count or head dim");
+    if (d->num_v_heads > 0) {
+        if (d->num_k_heads <= 0 || d->num_v_heads % d->num_k_heads != 0)
+            return fail(GDN_EINVAL, "num_v_heads %d must be a positive multiple of num_k_heads %d",
+                        d->num_v_heads, d->num_k_heads);
+        if (d->head_k_dim <= 0 || d->head_v_dim <= 0 || (d->head_k_dim & 3) || (d->head_v_dim & 3))
+            return fail(GDN_EINVAL, "head dims must be positive multiples of 4");
+        const int64_t c = 2LL * d->num_k_heads * d->head_k_dim +
+                          (int64_t)d->num_v_heads * d->head_v_dim;
+        if (c != d->conv_channels)
+            return fail(GDN_EINVAL, "conv_channels %d != 2*Hk*dk + Hv*dv = %lld",
+                        d->conv_channels, (long long)c);
+    }
+    if (!aligned16(d->page_stride_bytes) || !aligned16(d->conv_offset_bytes) ||
+        !aligned16(d->ssm_offset_bytes))
+        return fail(GDN_EALIGN, "page stride and region offsets must be multiples of 16 bytes");
+    const int64_t ssm = (int64_t)d->num_v_heads * d->head_k_dim * d->head_v_dim * 4;
+    const int64_t conv = (int64_t)(d->conv_width - 1) * d->conv_channels * 2;
+    if (d->conv_offset_bytes < 0 || d->ssm_offset_bytes < 0 ||
+        d->conv_offset_bytes + conv > d->page_stride_bytes ||
+        d->ssm_offset_bytes + ssm > d->page_stride_bytes)
+        return fail(GDN_ERANGE, "a region does not fit in the %lld-byte page",
+                    (long long)d->page_stride_bytes);
+    if (overlaps(d->conv_offset_bytes, conv, d->ssm_offset_bytes, ssm))
+        return fail(GDN_EOVERLAP, "window and state regions overlap");
+    int32_t n_linear = 0;
+    for (int32_t l = 0; l < d->num_layers; ++l) {
+        if (d->layer_base[l] == nullptr)
+            continue;
+        if (!aligned16(d->layer_base[l]))
+            return fail(GDN_EALIGN, "layer_base[%d] is not 16-byte aligned", l);
+        ++n_linear;
+    }
+    gdn_pool* p = new (std::nothrow) gdn_pool();
+    if (!p)
+        return fail(GDN_EINVAL, "out of host memory");
+    p->desc = *d;
+    p->bases.assign(d->layer_base, d->layer_base + d->num_layers);
+    p->desc.layer_base = p->bases.data();
+    for (int32_t l = 0; l < d->num_layers; ++l)
+        if (p->bases[l])
+            p->linear.push_back(l);
+    p->ssm_bytes = ssm;
+    p->conv_bytes = conv;
+    (void)n_linear;
+    *out = p;
+    return GDN_OK;
+}
+
+void gdn_pool_destroy(gdn_pool* pool) { delete pool; }
+
+int gdn_pool_region_bytes(const gdn_pool* pool, int64_t* ssm_bytes, int64_t* conv_bytes)
+{
+    if (!pool)
+        return fail(GDN_EINVAL, "pool is NULL");
+    if (ssm_bytes)
+        *ssm_bytes = pool->ssm_bytes;
+    if (conv_bytes)
+        *conv_bytes = pool->conv_bytes;
+    return GDN_OK;
+}
+
+int gdn_pool_describe(const gdn_pool* pool, char* buf, size_t len)
+{
+    if (!pool)
+        return fail(GDN_EINVAL, "pool is NULL");
+    const gdn_pool_desc& d = pool->desc;
+    std::string s;
+    char line[512];
+    const int64_t payload_end =
+        std::max(d.conv_offset_bytes + pool->conv_bytes, d.ssm_offset_bytes + pool->ssm_bytes);
+    snprintf(line, sizeof line,
+             "[gdn-pool] layers=%d (linear=%zu, attention-only=%zu) slots=%lld "
+             "page_stride=%lldB padding_after_payload=%lldB\n",
+             d.num_layers, pool->linear.size(), d.num_layers - pool->linear.size(),
+             (long long)d.num_slots, (long long)d.page_stride_bytes,
+             (long long)(d.page_stride_bytes - payload_end));
+    s += line;
+    snprintf(line, sizeof line,
+             "[gdn-pool] ssm: fp32 [Hv=%d][dk=%d][dv=%d] = %lldB at offset %lld, "
+             "slot stride %lld elements\n",
+             d.num_v_heads, d.head_k_dim, d.head_v_dim, (long long)pool->ssm_bytes,
+             (long long)d.ssm_offset_bytes, (long long)(d.page_stride_bytes / 4));
+    s += line;
+    snprintf(line, sizeof line,
+             "[gdn-pool] conv: bf16 [W-1=%d][C=%d] = %lldB at offset %lld, "
+             "slot stride %lld elements (Hk=%d)\n",
+             d.conv_width - 1, d.conv_channels, (long long)pool->conv_bytes,
+             (long long)d.conv_offset_bytes, (long long)(d.page_stride_bytes / 2),
+             d.num_k_heads);
+    s += line;
+    s += "[gdn-pool] attention-only layers:";
+    for (int32_t l = 0; l < d.num_layers; ++l)
+        if (!pool->bases[l]) {
+            snprintf(line, sizeof line, " %d", l);
+            s += line;
+        }
+    s += "\n";
+    if (buf && len > 0) {
+        size_t n = std::min(len - 1, s.size());
+        memcpy(buf, s.data(), n);
+        buf[n] = '\0';
+    }
+    return (int)s.size();
+}
+
+int gdn_restore_slots(const gdn_pool* pool, const gdn_restore_op* ops, int32_t n_ops,
+                      uint8_t* hs_dev, gdn_stream_t stream)
+{
+    gdn::clear_error();
+    if (!pool)
+        return fail(GDN_EINVAL, "pool is NULL");
+    if (n_ops < 0)
+        return fail(GDN_EINVAL, "n_ops < 0");
+    if (n_ops == 0)
+        return GDN_OK;
+    if (!ops || !hs_dev)
+        return fail(GDN_EINVAL, "ops and has_initial_state must not be NULL");
+    const int64_t ns = pool->desc.num_slots;
+    std::vector<gdn::HitPair> pairs;
+    std::vector<gdn::HsWrite> hs;
+    std::unordered_set<int32_t> dsts;
+    for (int32_t i = 0; i < n_ops; ++i) {
+        const gdn_restore_op& op = ops[i];
+        if (!op.requested)
+            continue;
+        if (op.src_slot < 0) {
+            hs.push_back({i, 0});
+            continue;
+        }
+        if (op.src_slot >= ns || op.dst_slot < 0 || op.dst_slot >= ns)
+            return fail(GDN_ERANGE, "op %d: dst %d / src %d outside [0, %lld)", i, op.dst_slot,
+                        op.src_slot, (long long)ns);
+        if (!dsts.insert(op.dst_slot).second)
+            return fail(GDN_EOVERLAP, "op %d: dst slot %d is named twice", i, op.dst_slot);
+        pairs.push_back({op.dst_slot, op.src_slot});
+        hs.push_back({i, pool->linear.empty() ? 0 : 1});
+    }
+    for (const gdn::HitPair& p : pairs)
+        if (dsts.count(p.src))
+            return fail(GDN_EOVERLAP, "src slot %d is also a dst slot", p.src);
+    const bool soft_failure = !pairs.empty() && pool->linear.empty();
+    if (pool->linear.empty())
+        pairs.clear();
+    int rc = gdn::launch_restore(pool, pairs, hs, hs_dev, reinterpret_cast<hipStream_t>(stream));
+    if (rc != GDN_OK)
+        return rc;
+    if (soft_failure)
+        return fail(GDN_WARN_COLD_FALLBACK,
+                    "no layer has a state pool: restored rows fall back to a cold start");
+    return GDN_OK;
+}
+
+int gdn_gather_states(const gdn_pool* pool, int32_t layer, const int32_t* idx, int32_t n,
+                      void* ssm_dense, void* conv_dense, gdn_stream_t stream)
+{
+    gdn::clear_error();
+    if (!pool)
+        return fail(GDN_EINVAL, "pool is NULL");
+    int rc = check_layer(pool, layer);
+    if (rc != GDN_OK)
+        return rc;
+    if (n < 0)
+        return fail(GDN_EINVAL, "n < 0");
+    if (n == 0)
+        return GDN_OK;
+    if (!idx || (pool->ssm_bytes > 0 && !ssm_dense) || !conv_dense)
+        return fail(GDN_EINVAL, "idx / dense buffers must not be NULL");
+    return gdn::launch_gather(pool, layer, idx, n, ssm_dense, conv_dense,
+                              reinterpret_cast<hipStream_t>(stream));
+}
+
+int gdn_scatter_states(const gdn_pool* pool, int32_t layer, const int32_t* idx, int32_t n,
+                       const void* ssm_dense, const void* conv_dense, gdn_stream_t stream)
+{
+    gdn::clear_error();
+    if (!pool)
+        return fail(GDN_EINVAL, "pool is NULL");
+    int rc = check_layer(pool, layer);
+    if (rc != GDN_OK)
+        return rc;
+    if (n < 0)
+        return fail(GDN_EINVAL, "n < 0");
+    if (n == 0)
+        return GDN_OK;
+    if (!idx || (pool->ssm_bytes > 0 && !ssm_dense) || !conv_dense)
+        return fail(GDN_EINVAL, "idx / dense buffers must not be NULL");
+    return gdn::launch_scatter(pool, layer, idx, n, ssm_dense, conv_dense,
+                               reinterpret_cast<hipStream_t>(stream));
+}
+
+int gdn_decode_step(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn_step_args* a,
+                    gdn_stream_t stream)
+{
+    gdn::clear_error();
+    if (!pool)
+        return fail(GDN_EINVAL, "pool is NULL");
+    if (rows < 0)
+        return fail(GDN_EINVAL, "rows < 0");
+    int rc = check_step_args(pool, layer, a);
+    if (rc != GDN_OK)
+        return rc;
+    const gdn_pool_desc& d = pool->desc;
+    if (!gdn::decode_supported(d.head_k_dim, d.head_v_dim, d.conv_width))
+        return fail(GDN_EUNSUPPORTED, "no decode kernel for dk=%d dv=%d W=%d", d.head_k_dim,
+                    d.head_v_dim, d.conv_width);
+    if (rows == 0)
+        return GDN_OK;
+    if (!aligned16(a->out) && ((reinterpret_cast<uintptr_t>(a->out) & 7u) != 0))
+        return fail(GDN_EALIGN, "out must be 8-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(a->x) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(a->conv_w) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(a->conv_b) & 3u) != 0)
+        return fail(GDN_EALIGN, "x, conv_w and conv_b must be 4-byte aligned");
+    return gdn::launch_decode(pool, layer, rows, a, reinterpret_cast<hipStream_t>(stream));
+}
+
+int gdn_prefill_varlen(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
+                       const int32_t* cu_seqlens, int32_t max_seqlen, int64_t total_tokens,
+                       const gdn_step_args* a, gdn_stream_t stream)
+{
+    gdn::clear_error();
+    if (!pool)
+        return fail(GDN_EINVAL, "pool is NULL");
+    if (num_seqs < 0 || max_seqlen < 0 || total_tokens < 0)
+        return fail(GDN_EINVAL, "negative num_seqs / max_seqlen / total_tokens");
+    int rc = check_step_args(pool, layer, a);
+    if (rc != GDN_OK)
+        return rc;
+    if (!cu_seqlens)
+        return fail(GDN_EINVAL, "cu_seqlens is NULL");
+    const gdn_pool_desc& d = pool->desc;
+    if (!gdn::prefill_supported(d.head_k_dim, d.head_v_dim, d.conv_width))
+        return fail(GDN_EUNSUPPORTED, "no prefill kernel for dk=%d dv=%d W=%d", d.head_k_dim,
+                    d.head_v_dim, d.conv_width);
+    if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0)
+        return GDN_OK;
+    if ((reinterpret_cast<uintptr_t>(a->out) & 7u) != 0)
+        return fail(GDN_EALIGN, "out must be 8-byte aligned");
+    return gdn::launch_prefill(pool, layer, num_seqs, cu_seqlens, a,
+                               reinterpret_cast<hipStream_t>(stream));
+}
+
+} // extern "C"

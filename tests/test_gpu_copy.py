@@ -1,0 +1,196 @@
+"""GPU parity of restore / gather / scatter against the oracle: bit-exact,
+padding and unselected pages included (via the C-ABI)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_linear_attention_slot_amd as gdn
+import oracle
+import workloads as wl
+from gpu_util import DevicePool, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_block_stride_example_on_gpu():
+    """The page's worked example: 48 bf16 per block in 128-byte pages; every
+    call touches elements [64 s, 64 s + 48) of the slots it names only."""
+    g = wl.Geometry(num_slots=6, C=16, W=4, Hk=0, Hv=0, dk=0, dv=0, page_stride=128, ssm_off=0,
+                    conv_off=0)
+    img = np.arange(6 * 64, dtype=np.uint16).view(np.uint8).reshape(6, 128).copy()
+    dp = DevicePool(g, [img])
+    idx = to_dev(np.arange(6, dtype=np.int32))
+    dense = torch.zeros((6, 96), dtype=torch.uint8, device="cuda")
+    log("gather 48-element blocks")
+    gdn.gdn_gather_states(dp.pool, 0, idx, 6, None, dense)
+    torch.cuda.synchronize()
+    got = dense.cpu().numpy().view(np.uint16)
+    for s in range(6):
+        assert np.array_equal(got[s], np.arange(64 * s, 64 * s + 48))
+    # scatter into slots 1 and 4, restore 5 -> 2
+    src = torch.full((2, 96), 0xFF, dtype=torch.uint8, device="cuda")
+    gdn.gdn_scatter_states(dp.pool, 0, to_dev(np.array([1, 4], np.int32)), 2, None, src)
+    hs = torch.zeros(1, dtype=torch.uint8, device="cuda")
+    assert gdn.gdn_restore_slots(dp.pool, [(2, 5, 1)], hs) == gdn.GDN_OK
+    torch.cuda.synchronize()
+    ref = img.copy()
+    oracle.scatter(ref, g, np.array([1, 4]), np.zeros((2, 0), np.uint8),
+                   np.full((2, 96), 0xFF, np.uint8))
+    h_ref = np.zeros(1, np.uint8)
+    oracle.restore([ref], g, np.array([[2, 5, 1]]), h_ref)
+    assert np.array_equal(dp.host(), ref)
+    assert hs.cpu().numpy()[0] == h_ref[0] == 1
+
+
+def tiny_layers(seed, n_layers, attention):
+    g = wl.tiny_geometry(extra_pad=128)
+    rng = wl.rng_for(seed)
+    imgs = [None if l in attention else wl.make_pool_image(g, rng, range(8), [])
+            for l in range(n_layers)]
+    return g, imgs
+
+
+def test_restore_truth_table_matches_oracle():
+    g, imgs = tiny_layers(40, 4, attention=(1, 3))
+    dp = DevicePool(g, imgs)
+    ops = np.array([[0, 3, 0], [4, -1, 1], [1, 5, 1], [2, 5, 1], [6, 7, 1]], np.int32)
+    hs0 = np.array([1, 1, 0, 0, 0], np.uint8)
+    hs = to_dev(hs0)
+    log("restore truth table")
+    assert gdn.gdn_restore_slots(dp.pool, ops.tolist(), hs) == gdn.GDN_OK
+    torch.cuda.synchronize()
+    ref = [None if im is None else im.copy() for im in imgs]
+    h_ref = hs0.copy()
+    assert oracle.restore(ref, g, ops, h_ref) == 0
+    assert np.array_equal(hs.cpu().numpy(), h_ref)
+    for l in (0, 2):
+        assert np.array_equal(dp.host(l), ref[l])
+
+
+def test_restore_soft_failure_all_attention():
+    g = wl.tiny_geometry()
+    dp = DevicePool(g, [None, None])
+    hs = to_dev(np.array([1, 1, 1], np.uint8))
+    rc = gdn.gdn_restore_slots(dp.pool, [(0, 3, 1), (1, -1, 1), (2, 4, 0)], hs)
+    torch.cuda.synchronize()
+    assert rc == gdn.GDN_WARN_COLD_FALLBACK
+    assert hs.cpu().numpy().tolist() == [0, 0, 1]
+
+
+def test_restore_many_ops_and_layers_split_launches():
+    """More ops and layers than one launch carries (kernel-argument budget)."""
+    g = wl.make_geometry(400, Hk=1, Hv=2, dk=16, dv=16, W=4, page_align=128, extra_pad=256)
+    rng = wl.rng_for(41)
+    n_layers = 40
+    imgs = [None if l % 4 == 3 else rng.integers(0, 256, (g.num_slots, g.page_stride),
+                                                dtype=np.uint8) for l in range(n_layers)]
+    dp = DevicePool(g, imgs)
+    perm = rng.permutation(g.num_slots)
+    n = 200
+    dst, pool_src = perm[:n], perm[n:]
+    src = np.where(rng.random(n) < 0.25, -1, rng.choice(pool_src, n))
+    req = (rng.random(n) < 0.9).astype(np.int32)
+    ops = np.stack([dst, src, req], axis=1).astype(np.int32)
+    hs0 = rng.integers(0, 2, n).astype(np.uint8)
+    hs = to_dev(hs0)
+    log(f"restore {n} ops x {n_layers} layers")
+    assert gdn.gdn_restore_slots(dp.pool, ops.tolist(), hs) == gdn.GDN_OK
+    torch.cuda.synchronize()
+    ref = [None if im is None else im.copy() for im in imgs]
+    h_ref = hs0.copy()
+    oracle.restore(ref, g, ops, h_ref)
+    assert np.array_equal(hs.cpu().numpy(), h_ref)
+    for l in range(n_layers):
+        if ref[l] is not None:
+            assert np.array_equal(dp.host(l), ref[l]), l
+
+
+@pytest.mark.parametrize("geom", ["tiny", "decode"])
+def test_gather_scatter_match_oracle(geom):
+    if geom == "tiny":
+        g = wl.tiny_geometry(extra_pad=128)
+    else:
+        g = wl.decode_geometry(num_slots=24, extra_pad=4096)
+    rng = wl.rng_for(42)
+    img = rng.integers(0, 256, (g.num_slots, g.page_stride), dtype=np.uint8)
+    dp = DevicePool(g, [img])
+    idx = np.array([3, -1, 7, g.num_slots, 0, 5], np.int32)
+    n = len(idx)
+    sd = torch.full((n, g.ssm_region_bytes), 0x5A, dtype=torch.uint8, device="cuda")
+    cd = torch.full((n, g.conv_region_bytes), 0x5A, dtype=torch.uint8, device="cuda")
+    log(f"gather/scatter {geom}")
+    gdn.gdn_gather_states(dp.pool, 0, to_dev(idx), n, sd, cd)
+    torch.cuda.synchronize()
+    rs, rc_ = oracle.gather(img, g, idx)
+    assert np.array_equal(sd.cpu().numpy(), rs)
+    assert np.array_equal(cd.cpu().numpy(), rc_)
+    new_s = rng.integers(0, 256, rs.shape, dtype=np.uint8)
+    new_c = rng.integers(0, 256, rc_.shape, dtype=np.uint8)
+    gdn.gdn_scatter_states(dp.pool, 0, to_dev(idx), n, to_dev(new_s), to_dev(new_c))
+    torch.cuda.synchronize()
+    ref = img.copy()
+    oracle.scatter(ref, g, idx, new_s, new_c)
+    assert np.array_equal(dp.host(), ref)
+
+
+def test_gather_unaligned_dense_rows():
+    """Region sizes that are not a multiple of 16 bytes use the element path."""
+    g = wl.make_geometry(6, Hk=1, Hv=1, dk=4, dv=4, W=3, C=10, page_align=128)
+    rng = wl.rng_for(43)
+    img = rng.integers(0, 256, (g.num_slots, g.page_stride), dtype=np.uint8)
+    dp = DevicePool(g, [img])
+    idx = np.array([5, 1, 2], np.int32)
+    sd = torch.zeros((3, g.ssm_region_bytes), dtype=torch.uint8, device="cuda")
+    cd = torch.zeros((3, g.conv_region_bytes), dtype=torch.uint8, device="cuda")
+    assert g.conv_region_bytes % 16 != 0
+    gdn.gdn_gather_states(dp.pool, 0, to_dev(idx), 3, sd, cd)
+    torch.cuda.synchronize()
+    rs, rc_ = oracle.gather(img, g, idx)
+    assert np.array_equal(sd.cpu().numpy(), rs)
+    assert np.array_equal(cd.cpu().numpy(), rc_)
+
+
+@pytest.mark.slow
+def test_restore_full_hybrid_stack():
+    """64-layer stack (every 4th layer attention-only), 48 GDN layers of 32 heads
+    x 128x128 fp32 + 8192-channel windows, 1024 slots with 4 KiB of non-zero
+    padding per page, 64 ops with a quarter misses.  Pages are checked on the
+    host for a sample of layers against the oracle run on those layers."""
+    g, linear, ops = wl.restore_workload(seed=0)
+    n_layers = len(linear)
+    log(f"allocating {int(linear.sum())} x {g.pool_bytes / 2**30:.1f} GiB")
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    bufs = []
+    for l in range(n_layers):
+        if not linear[l]:
+            bufs.append(None)
+            continue
+        b = torch.randint(0, 256, (g.num_slots, g.page_stride), dtype=torch.uint8,
+                          device="cuda", generator=gen)
+        b[:, g.conv_off + g.conv_region_bytes:] = wl.PAD_BYTE
+        bufs.append(b)
+    pool = gdn.gdn_pool_create(bufs, g.num_slots, g.page_stride, g.conv_off, g.ssm_off, g.C,
+                               g.W, g.Hk, g.Hv, g.dk, g.dv)
+    sample = [l for l in range(n_layers) if linear[l]][::12] + [n_layers - 2]
+    touched = np.unique(np.concatenate([ops[:, 0], ops[ops[:, 1] >= 0, 1]]))
+    before = {l: bufs[l][torch.from_numpy(touched).cuda()].cpu().numpy() for l in sample}
+    hs = torch.ones(len(ops), dtype=torch.uint8, device="cuda")
+    log("restore 64 ops x 48 layers")
+    assert gdn.gdn_restore_slots(pool, ops.tolist(), hs) == gdn.GDN_OK
+    torch.cuda.synchronize()
+    h_ref = np.ones(len(ops), np.uint8)
+    remap = {int(s): i for i, s in enumerate(touched)}
+    small = dataclasses.replace(g, num_slots=len(touched))
+    for l in sample:
+        ref = before[l].copy()
+        ops_small = np.array([[remap[d], remap[s] if s >= 0 else -1, r] for d, s, r in ops],
+                             np.int32)
+        h = np.ones(len(ops), np.uint8)
+        oracle.restore([ref], small, ops_small, h)
+        h_ref = h
+        got = bufs[l][torch.from_numpy(touched).cuda()].cpu().numpy()
+        assert np.array_equal(got, ref), l
+    assert np.array_equal(hs.cpu().numpy(), h_ref)
+    assert h_ref.sum() == (ops[:, 1] >= 0).sum()

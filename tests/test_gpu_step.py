@@ -1,0 +1,173 @@
+"""GPU parity of the decode step and the varlen prefill against the oracle
+(through the C-ABI).  Tolerances are those stated in gpu_util."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_linear_attention_slot_amd as gdn
+import oracle
+import workloads as wl
+from gpu_util import (DevicePool, check_outputs, check_pages, log, run_decode, run_prefill,
+                      u16)
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_layer(img, inp):
+    return oracle.gdn_layer(img, inp.geom, inp.cu_seqlens, inp.state_indices,
+                            inp.has_initial_state, inp.x, inp.conv_w, inp.conv_b, inp.alpha,
+                            inp.beta, inp.scale, inp.eps)
+
+
+def case(g, seed, lengths, warm, slots=None, bias=False, scale=1.0, long_memory=False,
+         sigma_s=0.5):
+    rng = wl.rng_for(seed)
+    n = len(lengths)
+    idx = rng.permutation(g.num_slots)[:n].astype(np.int32) if slots is None else \
+        np.asarray(slots, np.int32)
+    hs = np.asarray(warm, np.uint8)
+    valid = (idx >= 0) & (idx < g.num_slots)
+    img = wl.make_pool_image(g, rng, warm_slots=idx[valid & (hs == 1)],
+                             nan_slots=idx[valid & (hs == 0)], sigma_s=sigma_s)
+    inp = wl.step_inputs(g, rng, lengths, idx, hs, bias=bias, long_memory=long_memory)
+    inp.scale = scale
+    return inp, img
+
+
+def run_and_check(g, inp, img, mode, what):
+    dp = DevicePool(g, [img])
+    log(f"{what}: {mode} T={inp.total_tokens} N={inp.num_seqs}")
+    t = (run_decode if mode == "decode" else run_prefill)(dp, 0, inp)
+    torch.cuda.synchronize()
+    ref = img.copy()
+    o64, _ = oracle_layer(ref, inp)
+    e_out = check_outputs(u16(t["out"]), o64, what)
+    e_st = check_pages(g, dp.host(), ref, slots=inp.state_indices, what=what)
+    log(f"{what}: worst rel err out {e_out:.2e} state {e_st:.2e}")
+    return dp, t, ref
+
+
+DIMS = [(1, 2, 16), (2, 4, 32), (2, 2, 64), (4, 8, 128)]
+
+
+@pytest.mark.parametrize("Hk,Hv,d", DIMS)
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_decode_matches_oracle(Hk, Hv, d, W):
+    g = wl.make_geometry(12, Hk=Hk, Hv=Hv, dk=d, dv=d, W=W, page_align=128, extra_pad=128)
+    inp, img = case(g, 100 + d + W, [1] * 7, [1, 0, 1, 1, 0, 1, 1], bias=(W == 4), scale=0.7)
+    run_and_check(g, inp, img, "decode", f"decode d={d} W={W}")
+
+
+@pytest.mark.parametrize("Hk,Hv,d", DIMS)
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_prefill_matches_oracle(Hk, Hv, d, W):
+    g = wl.make_geometry(12, Hk=Hk, Hv=Hv, dk=d, dv=d, W=W, page_align=128, extra_pad=128)
+    # ragged lengths: several chunks, a ragged tail, shorter than the window, empty
+    lens = [70, 1, 33, 2, 0, 97, 32]
+    inp, img = case(g, 200 + d + W, lens, [1, 0, 1, 1, 0, 0, 1], bias=(W == 3), scale=0.7)
+    run_and_check(g, inp, img, "prefill", f"prefill d={d} W={W}")
+
+
+def test_padding_rows_and_out_of_range_slots():
+    g = wl.tiny_geometry(extra_pad=128)
+    inp, img = case(g, 7, [1, 1, 1, 1], [1, 1, 0, 1], slots=[2, -1, 5, 8])
+    _, t, _ = run_and_check(g, inp, img, "decode", "decode padding rows")
+    out = u16(t["out"])
+    assert (out[1] == 0).all() and (out[3] == 0).all()
+    inp, img = case(g, 8, [5, 3, 4], [1, 0, 1], slots=[-1, 4, 9])
+    _, t, _ = run_and_check(g, inp, img, "prefill", "prefill padding rows")
+    out = u16(t["out"])
+    assert (out[:5] == 0).all() and (out[8:] == 0).all()
+
+
+def test_tiny_config_continuation_on_gpu():
+    """4 seqs x 64 tokens from a cold start: 64 straight vs 32, restore into the
+    other four slots, 32 more -- bit-exact on the GPU and within tolerance of
+    the oracle; also as 32 decode steps after the restore."""
+    g = wl.tiny_geometry(extra_pad=128)
+    rng = wl.rng_for(0)
+    perm = rng.permutation(g.num_slots).astype(np.int32)
+    A, B = perm[:4], perm[4:]
+    img = wl.make_pool_image(g, rng, warm_slots=[], nan_slots=A)
+    full = wl.step_inputs(g, rng, [64] * 4, A, np.zeros(4, np.uint8), bias=True)
+
+    def part(t0, t1, slots, hs):
+        sel = np.concatenate([np.arange(i * 64 + t0, i * 64 + t1) for i in range(4)])
+        return dataclasses.replace(full, x=full.x[sel], alpha=full.alpha[sel],
+                                   beta=full.beta[sel], state_indices=np.asarray(slots, np.int32),
+                                   has_initial_state=np.asarray(hs, np.uint8),
+                                   cu_seqlens=np.arange(5, dtype=np.int32) * (t1 - t0))
+
+    straight = DevicePool(g, [img])
+    t_s = run_prefill(straight, 0, full)
+    split = DevicePool(g, [img])
+    run_prefill(split, 0, part(0, 32, A, [0] * 4))
+    hs = torch.ones(4, dtype=torch.uint8, device="cuda")
+    assert gdn.gdn_restore_slots(split.pool, [(int(b), int(a), 1) for a, b in zip(A, B)],
+                                 hs) == gdn.GDN_OK
+    t_2 = run_prefill(split, 0, part(32, 64, B, [1] * 4))
+    # the same continuation as 32 decode steps
+    dec = DevicePool(g, [img])
+    run_prefill(dec, 0, part(0, 32, A, [0] * 4))
+    gdn.gdn_restore_slots(dec.pool, [(int(b), int(a), 1) for a, b in zip(A, B)], hs)
+    dec_out = []
+    for t in range(32, 64):
+        dec_out.append(u16(run_decode(dec, 0, part(t, t + 1, B, [1] * 4))["out"]))
+    torch.cuda.synchronize()
+    o_s = u16(t_s["out"]).reshape(4, 64, g.Hv, g.dv)
+    o_2 = u16(t_2["out"]).reshape(4, 32, g.Hv, g.dv)
+    assert np.array_equal(o_2, o_s[:, 32:]), "restored continuation differs from straight run"
+    host_s, host_2 = straight.host(), split.host()
+    for a, b in zip(A, B):
+        assert np.array_equal(host_2[b][:g.conv_off + g.conv_region_bytes],
+                              host_s[a][:g.conv_off + g.conv_region_bytes])
+    # against the oracle
+    ref = img.copy()
+    o64, _ = oracle_layer(ref, full)
+    check_outputs(u16(t_s["out"]), o64, "tiny straight")
+    check_pages(g, host_s, ref, slots=A, what="tiny straight")
+    o64 = o64.reshape(4, 64, g.Hv, g.dv)
+    d = np.stack(dec_out, axis=1)  # [4, 32, Hv, dv]
+    check_outputs(d.reshape(-1, g.Hv, g.dv), o64[:, 32:].reshape(-1, g.Hv, g.dv),
+                  "tiny decode continuation")
+
+
+def test_decode_full_shape_matches_oracle():
+    """256 rows x 32 heads x 128x128 fp32, 1024-slot pool with 4 KiB pages,
+    90 % warm rows (the decode workload), all rows against the oracle."""
+    inp, pages = wl.decode_workload(seed=0)
+    g = inp.geom
+    log("decode workload: filling 1024-slot pool")
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    pool = torch.randint(0, 256, (g.num_slots, g.page_stride), dtype=torch.uint8, device="cuda",
+                         generator=gen)
+    idx_t = torch.from_numpy(inp.state_indices.astype(np.int64)).cuda()
+    pool[idx_t] = torch.from_numpy(pages).cuda()
+    others_before = pool[:64].clone()
+    dp = DevicePool.__new__(DevicePool)
+    dp.g, dp.bufs = g, [pool]
+    dp.pool = gdn.gdn_pool_create([pool], g.num_slots, g.page_stride, g.conv_off, g.ssm_off,
+                                  g.C, g.W, g.Hk, g.Hv, g.dk, g.dv)
+    t = run_decode(dp, 0, inp)
+    torch.cuda.synchronize()
+    got = pool[idx_t].cpu().numpy()
+    sub = dataclasses.replace(g, num_slots=inp.num_seqs)
+    ref = pages.copy()
+    loc = dataclasses.replace(inp, state_indices=np.arange(inp.num_seqs, dtype=np.int32),
+                              geom=sub)
+    o64, _ = oracle_layer(ref, loc)
+    e_out = check_outputs(u16(t["out"]), o64, "decode full")
+    e_st = check_pages(sub, got, ref, what="decode full")
+    log(f"decode full: worst rel err out {e_out:.2e} state {e_st:.2e}")
+    untouched = [s for s in range(64) if s not in set(inp.state_indices.tolist())]
+    assert torch.equal(pool[untouched], others_before[untouched])
+
+
+def test_prefill_varlen_full_shape_matches_oracle():
+    """8 sequences, lengths U{512..4096}, 16 heads x 128x128, half warm half cold."""
+    inp, img = wl.prefill_workload(seed=0)
+    g = inp.geom
+    log(f"prefill workload: lengths {np.diff(inp.cu_seqlens).tolist()}")
+    run_and_check(g, inp, img, "prefill", "prefill full")

@@ -125,12 +125,15 @@ def gdn_last_error() -> str:
 
 
 class Pool:
-    """Owner of a gdn_pool handle (host metadata only)."""
+    """Owner of a gdn_pool handle (host metadata only).  Holds references to
+    the layer buffers it was created from, so that tensors passed in stay
+    allocated while the pool can still name them."""
 
-    def __init__(self, handle: int, desc: gdn_pool_desc, bases):
+    def __init__(self, handle: int, desc: gdn_pool_desc, bases, tensors):
         self.handle = handle
         self.desc = desc
-        self._bases = bases  # keeps the ctypes array alive while the pool lives
+        self._bases = bases
+        self._tensors = tensors
 
     def close(self):
         if self.handle:
@@ -156,7 +159,7 @@ def gdn_pool_create(layer_base: Sequence, num_slots: int, page_stride_bytes: int
                       conv_width, num_k_heads, num_v_heads, head_k_dim, head_v_dim)
     h = C.c_void_p()
     _check(lib().gdn_pool_create(C.byref(d), C.byref(h)))
-    return Pool(h.value, d, bases)
+    return Pool(h.value, d, bases, list(layer_base))
 
 
 def gdn_pool_destroy(pool: Pool) -> None:
@@ -199,9 +202,13 @@ def gdn_scatter_states(pool: Pool, layer: int, idx, n: int, ssm_dense, conv_dens
 
 def make_step_args(x, conv_w, conv_b, alpha, beta, state_indices, has_initial_state, out,
                    scale=1.0, l2_eps=1e-6) -> gdn_step_args:
-    return gdn_step_args(_addr(x), _addr(conv_w), _addr(conv_b), _addr(alpha), _addr(beta),
-                         _addr(state_indices), _addr(has_initial_state), _addr(out),
-                         float(scale), float(l2_eps))
+    """The returned struct keeps references to the tensors it names, so that
+    temporaries passed here stay allocated as long as the struct lives."""
+    a = gdn_step_args(_addr(x), _addr(conv_w), _addr(conv_b), _addr(alpha), _addr(beta),
+                      _addr(state_indices), _addr(has_initial_state), _addr(out),
+                      float(scale), float(l2_eps))
+    a._keep = (x, conv_w, conv_b, alpha, beta, state_indices, has_initial_state, out)
+    return a
 
 
 def gdn_decode_step(pool: Pool, layer: int, rows: int, args: gdn_step_args, stream=None) -> int:

@@ -137,19 +137,25 @@ def test_gather_scatter_match_oracle(geom):
 
 def test_gather_unaligned_dense_rows():
     """Region sizes that are not a multiple of 16 bytes use the element path."""
-    g = wl.make_geometry(6, Hk=1, Hv=1, dk=4, dv=4, W=3, C=10, page_align=128)
+    # conv-window-only pool: 2 x 10 bf16 = 40 bytes per page
+    g = wl.Geometry(num_slots=6, C=10, W=3, Hk=0, Hv=0, dk=0, dv=0, page_stride=128, ssm_off=0,
+                    conv_off=0)
     rng = wl.rng_for(43)
     img = rng.integers(0, 256, (g.num_slots, g.page_stride), dtype=np.uint8)
     dp = DevicePool(g, [img])
     idx = np.array([5, 1, 2], np.int32)
-    sd = torch.zeros((3, g.ssm_region_bytes), dtype=torch.uint8, device="cuda")
     cd = torch.zeros((3, g.conv_region_bytes), dtype=torch.uint8, device="cuda")
     assert g.conv_region_bytes % 16 != 0
-    gdn.gdn_gather_states(dp.pool, 0, to_dev(idx), 3, sd, cd)
+    gdn.gdn_gather_states(dp.pool, 0, to_dev(idx), 3, None, cd)
     torch.cuda.synchronize()
-    rs, rc_ = oracle.gather(img, g, idx)
-    assert np.array_equal(sd.cpu().numpy(), rs)
+    _, rc_ = oracle.gather(img, g, idx)
     assert np.array_equal(cd.cpu().numpy(), rc_)
+    new_c = rng.integers(0, 256, rc_.shape, dtype=np.uint8)
+    gdn.gdn_scatter_states(dp.pool, 0, to_dev(idx), 3, None, to_dev(new_c))
+    torch.cuda.synchronize()
+    ref = img.copy()
+    oracle.scatter(ref, g, idx, np.zeros((3, 0), np.uint8), new_c)
+    assert np.array_equal(dp.host(), ref)
 
 
 @pytest.mark.slow

@@ -174,6 +174,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-restore", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (3 times), the known-size "
+                         "reference that scales the FETCH_SIZE / WRITE_SIZE counters")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU only: the slot-state path has no cross-GPU step "
@@ -185,6 +188,14 @@ def main():
     import hybrid_linear_attention_slot_amd as gdn
     gdn.lib()
 
+    if a.calibrate:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     inp, ms, nbytes = bench_decode(a.steps, a.warmup)
     gbs = nbytes / (ms * 1e-3) / 1e9
     pinp, pms = bench_prefill(a.steps, a.warmup)

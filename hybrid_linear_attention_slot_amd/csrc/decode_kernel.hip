@@ -64,12 +64,51 @@ struct DecodeParams {
     float eps;
 };
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over one page's state region.  Buffer instructions take the
+// per-key offset in an SGPR, so a lane needs a single VGPR offset for all of
+// its loads and stores, and the hardware drops accesses past num_records.
+constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer, gfx9-family layout
+constexpr int kNonTemporal = 2;          // cache-policy bit: streamed once
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(float* ssm, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(ssm, short(0), bytes, kBufferWord3);
+}
+
+// Tile of head h: key rows jl + LPC*m, value columns i0..i0+3 (voff = byte
+// offset of (jl, i0) inside a head tile).
 template <int DK, int DV, int JPL, int LPC>
-__device__ __forceinline__ void load_tile(float4 (&s)[JPL], const float* tile, int jl, int i0)
+__device__ __forceinline__ void load_tile(f32x4 (&s)[JPL], __amdgpu_buffer_rsrc_t r, int voff,
+                                          int h)
 {
 #pragma unroll
     for (int m = 0; m < JPL; ++m)
-        s[m] = *reinterpret_cast<const float4*>(tile + (jl + LPC * m) * DV + i0);
+        s[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             r, voff, (h * DK + LPC * m) * DV * 4, kNonTemporal));
+}
+
+// Stores take their whole offset in the VGPR and a literal zero soffset:
+// the compiler only protects a 128-bit store's data registers from being
+// overwritten too early (the store reads them after issue) when soffset is
+// not an SGPR, and with an SGPR soffset that window was seen to corrupt the
+// last lanes' data.
+template <int DK, int DV, int LPC>
+__device__ __forceinline__ void store_row(const f32x4& t, __amdgpu_buffer_rsrc_t r, int voff,
+                                          int h, int m)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t), r,
+                                           voff + (h * DK + LPC * m) * DV * 4, 0, kNonTemporal);
+}
+
+template <int JPL>
+__device__ __forceinline__ void zero_tile(f32x4 (&s)[JPL])
+{
+#pragma unroll
+    for (int m = 0; m < JPL; ++m)
+        s[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Conv inputs of one pair of adjacent channels (c, c+1), kept as the raw
@@ -152,6 +191,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, i
     const int h0 = g * G;
     uint16_t* out_row = p.out + (int64_t(row) * p.Hv + h0) * DV;
     float* ssm = reinterpret_cast<float*>(page + p.ssm_off);
+    const __amdgpu_buffer_rsrc_t rs = state_rsrc(ssm, p.Hv * DK * DV * 4);
+    const int voff = (jl * DV + i0) * 4;
     uint16_t* win = reinterpret_cast<uint16_t*>(page + p.conv_off);
     const int C = p.C;
 
@@ -165,21 +206,23 @@ __device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, i
         return 2 * p.Hk * DK + h0 * DV + (vc - 2 * DK);
     };
 
-    // 1. conv inputs of the first channel pair, then the first head's state
-    //    tile: loads complete in issue order, so the conv can start while the
-    //    tile is still in flight
+    // 1. conv inputs of the first channel pair, then the state tiles of the
+    //    first two heads: loads complete in issue order, so the conv runs
+    //    while the tiles are in flight, and the second tile arrives while
+    //    the first head is being processed
     ConvPairIn<W> cin;
     const int vc0 = 2 * tid;
     const int c0 = chan(vc0 < nvc ? vc0 : 0);
     if (vc0 < nvc)
         load_conv_pair<W>(cin, p, row, c0, reinterpret_cast<const uint32_t*>(win + c0), WARM);
-    float4 s[JPL];
+    f32x4 s0[JPL], s1[JPL];
     if constexpr (WARM) {
-        load_tile<DK, DV, JPL, LPC>(s, ssm + int64_t(h0) * DK * DV, jl, i0);
+        load_tile<DK, DV, JPL, LPC>(s0, rs, voff, h0);
+        if (G > 1)
+            load_tile<DK, DV, JPL, LPC>(s1, rs, voff, h0 + 1);
     } else {
-#pragma unroll
-        for (int m = 0; m < JPL; ++m)
-            s[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+        zero_tile<JPL>(s0);
+        zero_tile<JPL>(s1);
     }
 
     // 2. conv + SiLU; groups with more channels than 2 per thread loop on
@@ -193,7 +236,9 @@ __device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, i
     }
     __syncthreads();
 
-    // 3. L2 norms and k.q; every wave reduces redundantly (no second barrier)
+    // 3. L2 norms and k.q; every wave reduces redundantly (no second barrier).
+    //    The dot products below run on the raw conv outputs; the norm factors
+    //    are applied to their sums.
     float sq = 0.f, sk = 0.f, qk = 0.f;
     for (int j = lane; j < DK; j += 64) {
         const float a = ys[j], b = ys[DK + j];
@@ -207,33 +252,17 @@ __device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, i
     const float rq = p.scale / sqrtf(sq + p.eps);
     const float rk = 1.0f / sqrtf(sk + p.eps);
     const float kq = qk * rq * rk;
-    float kh[JPL], qh[JPL];
-#pragma unroll
-    for (int m = 0; m < JPL; ++m) {
-        const int j = jl + LPC * m;
-        qh[m] = ys[j] * rq;
-        kh[m] = ys[DK + j] * rk;
-    }
+    const float* qy = ys + jl;      // raw q of key jl + LPC*m at qy[LPC*m]
+    const float* ky = ys + DK + jl; // raw k likewise
 
-    // 4. gated delta rule, one v-head after another
-    for (int hh = 0; hh < G; ++hh) {
+    // 4. gated delta rule for one v-head on the tile held in s
+    auto head = [&](f32x4 (&s)[JPL], int hh) {
         const int h = h0 + hh;
-        float* tile = ssm + int64_t(h) * DK * DV;
-        if constexpr (WARM) {
-            if (hh > 0)
-                load_tile<DK, DV, JPL, LPC>(s, tile, jl, i0);
-        }
-        float4 u = make_float4(0.f, 0.f, 0.f, 0.f), o = u;
+        f32x4 u = f32x4{0.f, 0.f, 0.f, 0.f}, o = u;
 #pragma unroll
         for (int m = 0; m < JPL; ++m) {
-            u.x += s[m].x * kh[m];
-            u.y += s[m].y * kh[m];
-            u.z += s[m].z * kh[m];
-            u.w += s[m].w * kh[m];
-            o.x += s[m].x * qh[m];
-            o.y += s[m].y * qh[m];
-            o.z += s[m].z * qh[m];
-            o.w += s[m].w * qh[m];
+            u += s[m] * ky[LPC * m];
+            o += s[m] * qy[LPC * m];
         }
         u.x = group_sum<LPC>(u.x);
         u.y = group_sum<LPC>(u.y);
@@ -245,28 +274,27 @@ __device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, i
         o.w = group_sum<LPC>(o.w);
         const float a = p.alpha[int64_t(row) * p.Hv + h];
         const float b = p.beta[int64_t(row) * p.Hv + h];
-        const float* v = ys + 2 * DK + hh * DV + i0;
-        float4 d;
-        d.x = b * (v[0] - a * u.x);
-        d.y = b * (v[1] - a * u.y);
-        d.z = b * (v[2] - a * u.z);
-        d.w = b * (v[3] - a * u.w);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ys + 2 * DK + hh * DV + i0);
+        // d = b (v - a S k^), with k^ = rk k
+        const f32x4 d = b * (v - (a * rk) * u);
+        const f32x4 dk = d * rk; // update S <- a S + d k^T with raw k
 #pragma unroll
         for (int m = 0; m < JPL; ++m) {
-            float4 t;
-            t.x = fmaf(d.x, kh[m], a * s[m].x);
-            t.y = fmaf(d.y, kh[m], a * s[m].y);
-            t.z = fmaf(d.z, kh[m], a * s[m].z);
-            t.w = fmaf(d.w, kh[m], a * s[m].w);
-            *reinterpret_cast<float4*>(tile + (jl + LPC * m) * DV + i0) = t;
+            store_row<DK, DV, LPC>(a * s[m] + dk * ky[LPC * m], rs, voff, h, m);
         }
         if (jl == 0) {
-            const float o0 = fmaf(d.x, kq, a * o.x);
-            const float o1 = fmaf(d.y, kq, a * o.y);
-            const float o2 = fmaf(d.z, kq, a * o.z);
-            const float o3 = fmaf(d.w, kq, a * o.w);
-            *reinterpret_cast<uint2*>(out_row + hh * DV + i0) = pack_bf16x4(o0, o1, o2, o3);
+            // o = a S q^ + d (k^.q^), with q^ = rq q
+            const f32x4 ov = (a * rq) * o + d * kq;
+            *reinterpret_cast<uint2*>(out_row + hh * DV + i0) = pack_bf16x4(ov.x, ov.y, ov.z, ov.w);
         }
+    };
+    head(s0, 0);
+    if (G > 1)
+        head(s1, 1);
+    for (int hh = 2; hh < G; ++hh) { // groups wider than two heads: one tile at a time
+        if constexpr (WARM)
+            load_tile<DK, DV, JPL, LPC>(s0, rs, voff, h0 + hh);
+        head(s0, hh);
     }
 }
 

@@ -54,6 +54,33 @@ def prefill_bytes(inp) -> int:
             + g.C * g.W * 2 + 9 * n)
 
 
+DECODE_SOURCES = ("hybrid_linear_attention_slot_amd/csrc/decode_kernel.hip",
+                  "hybrid_linear_attention_slot_amd/csrc/device_utils.h")
+DECODE_PROFILE = "profiles/decode_kernel_256rows_32heads_128x128.md"
+
+
+def measured_traffic(profile: str, sources) -> "int | None":
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary of
+    the kernel, or None when the kernel sources have changed since the
+    counters were taken (the summary records the sources' sha256)."""
+    import hashlib
+    path = os.path.join(ROOT, profile)
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for s in sources:
+        with open(os.path.join(ROOT, s), "rb") as f:
+            h.update(f.read())
+    nbytes = digest = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic_bytes_per_launch:"):
+                nbytes = int(line.split(":")[1])
+            elif line.startswith("source_sha256:"):
+                digest = line.split(":")[1].split()[0]
+    return nbytes if digest == h.hexdigest() else None
+
+
 def timed(fn, steps, warmup, stream):
     import torch
     for _ in range(warmup):
@@ -231,7 +258,8 @@ def main():
                    "rows": inp.num_seqs, "warm_rows": int(inp.has_initial_state.sum()),
                    "bytes_per_step": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(DECODE_PROFILE, DECODE_SOURCES)},
         "prefill": prefill,
         "restore": restore,
     }

@@ -273,3 +273,56 @@ def restore_workload(seed=0, num_layers=64, attn_every=4, n_ops=64, miss_frac=0.
     src = np.where(miss, -1, src)
     ops = np.stack([dst, src, np.ones(n_ops, dtype=np.int64)], axis=1).astype(np.int32)
     return g, linear, ops
+
+
+# ---------------------------------------------------------------------------
+# Device-side draws for workloads too large to draw on the host (the
+# continuation run at scale).  Same distributions as above, drawn with a
+# seeded torch generator on the GPU; the oracle receives host copies of the
+# parts it checks.
+# ---------------------------------------------------------------------------
+def device_generator(*seed_parts):
+    import torch
+    s = 0
+    for p in seed_parts:
+        s = (s * 1_000_003 + int(p)) % (1 << 62)
+    return torch.Generator(device="cuda").manual_seed(s)
+
+
+def device_x(gen, n_tok, C):
+    """x ~ N(0,1) rounded to bf16 (RNE); returned as an int16 tensor of bf16 bits."""
+    import torch
+    return torch.randn((n_tok, C), generator=gen, device="cuda",
+                       dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+
+
+def device_gates(gen, n_tok, Hv, long_memory=False):
+    import torch
+    za = torch.randn((n_tok, Hv), generator=gen, device="cuda", dtype=torch.float64)
+    zb = torch.randn((n_tok, Hv), generator=gen, device="cuda", dtype=torch.float64)
+    alpha = torch.exp(-(0.01 if long_memory else 1.0) * torch.nn.functional.softplus(za))
+    beta = torch.sigmoid(zb)
+    return alpha.to(torch.float32).contiguous(), beta.to(torch.float32).contiguous()
+
+
+def device_fill_warm(buf, g: Geometry, slots, gen, sigma_s=0.1):
+    """Warm payloads for `slots` of a device pool buffer [num_slots, page_stride]:
+    state ~ N(0, sigma_s) fp32, window ~ N(0,1) bf16."""
+    import torch
+    idx = torch.as_tensor(np.asarray(slots, np.int64), device="cuda")
+    n = idx.numel()
+    s = torch.randn((n, g.ssm_region_bytes // 4), generator=gen, device="cuda") * sigma_s
+    w = torch.randn((n, g.conv_region_bytes // 2), generator=gen, device="cuda")
+    w = w.to(torch.bfloat16)
+    buf[idx, g.ssm_off:g.ssm_off + g.ssm_region_bytes] = s.view(torch.uint8)
+    buf[idx, g.conv_off:g.conv_off + g.conv_region_bytes] = w.view(torch.uint8)
+
+
+def device_fill_nan(buf, g: Geometry, slots):
+    import torch
+    idx = torch.as_tensor(np.asarray(slots, np.int64), device="cuda")
+    s = torch.full((idx.numel(), g.ssm_region_bytes // 4), float("nan"), device="cuda")
+    w = torch.full((idx.numel(), g.conv_region_bytes // 2), 0x7FC0, dtype=torch.int16,
+                   device="cuda")
+    buf[idx, g.ssm_off:g.ssm_off + g.ssm_region_bytes] = s.view(torch.uint8)
+    buf[idx, g.conv_off:g.conv_off + g.conv_region_bytes] = w.view(torch.uint8)

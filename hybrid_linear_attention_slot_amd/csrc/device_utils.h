@@ -32,9 +32,11 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
     return r;
 }
 
+// x * sigmoid(x) with the hardware reciprocal (about 1 ulp); for x -> -inf the
+// exponential overflows to +inf and the result is -0.
 __device__ __forceinline__ float silu(float x)
 {
-    return x / (1.0f + __expf(-x));
+    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
 // DPP lane permutations (all source lanes valid, so `old` is never used).

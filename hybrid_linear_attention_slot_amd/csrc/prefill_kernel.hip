@@ -9,19 +9,29 @@
 // token does not grow with the history), and the final window and state are
 // scattered back into the same page ("非连续 KV Cache" §5-§6).
 //
-// Parallel structure: every value row of a head's state evolves on its own
-// once k, q, v, a, b of the token are known, so a workgroup takes one
-// (sequence, v-head, slice of ISZ value rows).  Its waves never exchange
-// partial sums: a wave owns 4*NCW value columns for all dk keys, the LPC
-// lanes that share a float4 column split the keys, and S k / S q are finished
-// with DPP sums inside the wave.  The sequence is processed in chunks of CT
-// tokens:
-//   A. stage the chunk's raw inputs of the workgroup's channels (q and k of
-//      its k-head, v of its slice) into LDS with coalesced loads (as fp32);
-//   B. conv + SiLU per channel, the W-1 previous inputs held in registers;
-//   C. per token: L2 norms of q and k and k.q (one wave per token);
-//   D. the serial recurrence over the chunk's tokens, reading k^, q^, v, a, b
-//      from LDS; no barrier inside the chunk.
+// Parallel structure.  Every value column of a head's state evolves on its
+// own once k, q, v, a, b of the token are known, so a workgroup takes one
+// (sequence, v-head, slice of ISZ value columns) and keeps that slice of the
+// state in registers for the whole sequence.  Its waves have two roles:
+//   - consumer waves run the serial recurrence.  A lane holds KPL keys of one
+//     value column (keys 4 jl + 4 LPC m + e, so that the LPC lanes of a
+//     column read one contiguous run of k or q from LDS); S k and S q are
+//     lane-partial dot products finished with DPP sums over the LPC lanes,
+//     and  o = a (S_old q^) + d (k^.q^),  d = b (v - a S_old k^),  so one pass
+//     over the state gives both the update and the output;
+//   - producer waves prepare the next chunk of CT tokens while the consumers
+//     work on the current one: they stage the raw inputs of the workgroup's
+//     channels (q and k of its k-head, v of its slice) in an LDS ring with
+//     coalesced 16-byte loads issued a chunk ahead, run the conv + SiLU, form
+//     the per-token norm factors, and write the previous chunk's outputs to
+//     HBM as bf16.
+// Consumers and producers meet at one barrier per chunk; the per-token work
+// on the critical path is the consumers' recurrence alone.  The L2 norm
+// factors are applied to the reduced sums, so k and q stay raw in LDS.
+// Every arithmetic step of a token is the same wherever the chunk boundaries
+// fall, so a run split at any token and resumed from the written-back state
+// gives the same bits as the straight run.
+//
 // The conv window is rewritten by a second small kernel after this one, so
 // that no workgroup of a sequence can overwrite the window another workgroup
 // of the same sequence has yet to read.
@@ -35,17 +45,28 @@ namespace {
 
 template <int DK, int DV>
 struct PrefillShape {
-    static constexpr int NCW = (DV / 4) < 4 ? (DV / 4) : 4;   // float4 columns per wave
-    static constexpr int LPC = 64 / NCW;                      // lanes splitting one column's keys
-    static constexpr int JPL = DK / LPC;                      // keys per lane
-    static constexpr int NWP = (DV / (4 * NCW)) < 2 ? (DV / (4 * NCW)) : 2; // waves per workgroup
-    static constexpr int ISZ = 4 * NCW * NWP;                 // value rows per workgroup
-    static constexpr int NSL = DV / ISZ;                      // slices per head
-    static constexpr int NT = 64 * NWP;
-    static constexpr int NCH = 2 * DK + ISZ;                  // channels per workgroup
-    static constexpr int CPT = (NCH + NT - 1) / NT;           // channel slots per thread
-    static constexpr int CT = 32;                             // tokens per chunk
-    static_assert(JPL >= 1 && DK % LPC == 0 && DV % ISZ == 0, "unsupported head dims");
+    static constexpr int KPL = DK >= 64 ? 16 : (DK >= 32 ? 8 : 4); // keys per consumer lane
+    static constexpr int LPC = DK / KPL;                            // lanes sharing one column
+    static constexpr int CPW = 64 / LPC;                            // columns per consumer wave
+    static constexpr int NCONS = (DV / CPW) < 4 ? (DV / CPW) : 4;   // consumer waves
+    static constexpr int NPROD = 2;                                 // producer waves
+    static constexpr int ISZ = NCONS * CPW;                         // value columns per workgroup
+    static constexpr int NSL = DV / ISZ;                            // workgroups per head
+    static constexpr int NT = 64 * (NCONS + NPROD);
+    static constexpr int CT = 16;                                   // tokens per chunk
+    static constexpr int RING = 3 * CT;                             // staged input rows
+    static constexpr int NCH = 2 * DK + ISZ;                        // channels: q | k | v slice
+    static constexpr int NPIECE = NCH / 8;                          // 16-byte pieces per row
+    static constexpr int QKP = DK / 2;                              // q (and k) channel pairs
+    static constexpr int NQK = (QKP + 63) / 64;                     // q/k pair slots per lane
+    static constexpr int NVP = ISZ / 2;                             // v channel pairs
+    static constexpr int NVS = (NVP + 63) / 64;                     // v pair slots per lane
+    static constexpr int PLANES = 64 * NPROD;
+    static constexpr int LOADS = (CT * NPIECE + PLANES - 1) / PLANES; // pieces per producer lane
+    static constexpr int OPR = ISZ / 8;                             // 8-column output pieces per row
+    static_assert(DK == DV, "square heads only");
+    static_assert(KPL % 4 == 0 && DK % KPL == 0 && LPC >= 1 && LPC <= 64, "key split");
+    static_assert(NCONS >= 1 && DV % ISZ == 0 && ISZ % 8 == 0, "column split");
 };
 
 struct PrefillParams {
@@ -58,6 +79,8 @@ struct PrefillParams {
     int32_t C;
     int32_t Hk;
     int32_t Hv;
+    int32_t x_vec;   // x is 16-byte aligned
+    int32_t out_vec; // out is 16-byte aligned
     const int32_t* cu;
     const uint16_t* x;
     const uint16_t* conv_w;
@@ -71,188 +94,314 @@ struct PrefillParams {
     float eps;
 };
 
+__device__ __forceinline__ float lo_bf16(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+template <int RING>
+__device__ __forceinline__ int ring_pos(int t) // t >= -RING
+{
+    return (t + RING) % RING;
+}
+
 template <int DK, int DV, int W>
 __global__ __launch_bounds__((PrefillShape<DK, DV>::NT)) void prefill_kernel(PrefillParams p)
 {
     using Sh = PrefillShape<DK, DV>;
-    constexpr int JPL = Sh::JPL, LPC = Sh::LPC, NCH = Sh::NCH, CT = Sh::CT, NT = Sh::NT;
-    // q | k | v-slice per token: raw inputs after phase A, conv outputs after
-    // phase B (each thread reads and rewrites only its own channels), q and k
-    // normalised in place by phase C
-    __shared__ __align__(16) float ys[CT][NCH];
-    __shared__ float s_kq[CT], s_a[CT], s_b[CT];
+    constexpr int KPL = Sh::KPL, LPC = Sh::LPC, CPW = Sh::CPW, NCONS = Sh::NCONS;
+    constexpr int ISZ = Sh::ISZ, NCH = Sh::NCH, CT = Sh::CT, RING = Sh::RING;
+    constexpr int NT = Sh::NT, PLANES = Sh::PLANES, NPIECE = Sh::NPIECE, QKP = Sh::QKP;
 
+    __shared__ __align__(16) uint16_t raw[RING][NCH];  // staged raw inputs, row = token % RING
+    __shared__ __align__(16) float ys[2][CT][NCH];     // conv outputs (raw q | raw k | v)
+    __shared__ __align__(16) float sc[2][CT][8];       // a, b, rk, rq, k^.q^ per token
+    __shared__ __align__(8) float gab[RING][2];        // staged alpha, beta
+    __shared__ __align__(16) float ob[2][CT][ISZ];     // outputs of a chunk (fp32)
+
+    // workgroup -> (k-head g, sequence n, v-head of the group, slice): the
+    // workgroups of one (n, g) read the same q/k inputs and share an XCD
+    const int G = p.Hv / p.Hk;
     const int nblocks = p.num_seqs * p.Hv * Sh::NSL;
     const int id = xcd_contiguous_id(blockIdx.x, nblocks);
-    const int sl = id % Sh::NSL;
-    const int h = (id / Sh::NSL) % p.Hv;
-    const int n = id / (Sh::NSL * p.Hv);
-    const int G = p.Hv / p.Hk;
-    const int g = h / G;
+    const int per_g = p.num_seqs * G * Sh::NSL;
+    const int g = id / per_g;
+    const int r0 = id - g * per_g;
+    const int n = r0 / (G * Sh::NSL);
+    const int r1 = r0 - n * (G * Sh::NSL);
+    const int h = g * G + r1 / Sh::NSL;
+    const int sl = r1 % Sh::NSL;
+
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int jl = lane % LPC;
-    const int il = 4 * (wave * Sh::NCW + lane / LPC); // value column inside the slice
-    const int i0 = sl * Sh::ISZ + il;                  // value column inside the head
-
     const int tb = p.cu[n];
     const int L = p.cu[n + 1] - tb;
     if (L <= 0)
         return;
-    const int64_t out_stride = int64_t(p.Hv) * DV;
-    uint16_t* out = p.out + int64_t(tb) * out_stride + int64_t(h) * DV + i0;
+    const int64_t out_tok = int64_t(p.Hv) * DV; // out elements per token
+    uint16_t* out_base = p.out + int64_t(tb) * out_tok + int64_t(h) * DV + sl * ISZ;
     const int slot = p.state_indices[n];
     if (slot < 0 || slot >= p.num_slots) { // padding row: zero outputs, no state I/O
-        if (jl == 0)
-            for (int t = 0; t < L; ++t)
-                *reinterpret_cast<uint2*>(out + t * out_stride) = make_uint2(0u, 0u);
+        for (int e = tid; e < L * (ISZ / 4); e += NT) {
+            const int tt = e / (ISZ / 4), c4 = e - tt * (ISZ / 4);
+            *reinterpret_cast<uint2*>(out_base + tt * out_tok + 4 * c4) = make_uint2(0u, 0u);
+        }
         return;
     }
     const bool warm = p.hs[n] != 0;
     uint8_t* page = p.layer + int64_t(slot) * p.page_stride;
-    float* tile = reinterpret_cast<float*>(page + p.ssm_off) + int64_t(h) * DK * DV;
-    const uint16_t* win = reinterpret_cast<const uint16_t*>(page + p.conv_off);
+    const int nchunks = (L + CT - 1) / CT;
 
-    // the workgroup's channel -> global conv channel
+    // global channel of the workgroup's channel `ch` (q | k | v slice)
     auto chan = [&](int ch) -> int {
         if (ch < DK)
             return g * DK + ch;
         if (ch < 2 * DK)
             return p.Hk * DK + g * DK + (ch - DK);
-        return 2 * p.Hk * DK + h * DV + sl * Sh::ISZ + (ch - 2 * DK);
+        return 2 * p.Hk * DK + h * DV + sl * ISZ + (ch - 2 * DK);
     };
+    auto chunk_len = [&](int k) { return min(CT, L - k * CT); };
 
-    // state slice into registers
-    float4 s[JPL];
+    if (wave < NCONS) {
+        // ======================= consumer waves =============================
+        const int col = wave * CPW + lane / LPC; // value column inside the slice
+        const int jl = lane % LPC;
+        const int gcol = sl * ISZ + col;
+        float* tile = reinterpret_cast<float*>(page + p.ssm_off) + int64_t(h) * DK * DV;
+        float s[KPL];
 #pragma unroll
-    for (int m = 0; m < JPL; ++m)
-        s[m] = warm ? *reinterpret_cast<const float4*>(tile + (jl + LPC * m) * DV + i0)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
-
-    // per-thread conv channels: taps, bias and the last W-1 inputs
-    float cw[Sh::CPT][W], cb[Sh::CPT], cwin[Sh::CPT][W > 1 ? W - 1 : 1];
+        for (int m = 0; m < KPL / 4; ++m)
 #pragma unroll
-    for (int k = 0; k < Sh::CPT; ++k) {
-        const int ch = tid + k * NT;
-        const int c = chan(ch < NCH ? ch : 0);
+            for (int e = 0; e < 4; ++e)
+                s[4 * m + e] = warm ? tile[(4 * jl + 4 * LPC * m + e) * DV + gcol] : 0.f;
+        __syncthreads(); // A: history and chunk 0 staged
+        __syncthreads(); // B: chunk 0 prepared
+        for (int c = 0; c < nchunks; ++c) {
+            const int buf = c & 1;
+            const int nt = chunk_len(c);
+            for (int tt = 0; tt < nt; ++tt) {
+                const float* yt = ys[buf][tt];
+                const float4 g4 = *reinterpret_cast<const float4*>(sc[buf][tt]);
+                const float kq = sc[buf][tt][4];
+                float kr[KPL];
+                float u0 = 0.f, u1 = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
-        for (int w = 0; w < W; ++w)
-            cw[k][w] = bf16_to_f32(p.conv_w[int64_t(c) * W + w]);
-        cb[k] = p.conv_b ? bf16_to_f32(p.conv_b[c]) : 0.f;
+                for (int m = 0; m < KPL / 4; ++m) {
+                    const float4 kk = *reinterpret_cast<const float4*>(yt + DK + 4 * jl + 4 * LPC * m);
+                    const float4 qq = *reinterpret_cast<const float4*>(yt + 4 * jl + 4 * LPC * m);
+                    kr[4 * m + 0] = kk.x;
+                    kr[4 * m + 1] = kk.y;
+                    kr[4 * m + 2] = kk.z;
+                    kr[4 * m + 3] = kk.w;
+                    u0 = fmaf(s[4 * m + 0], kk.x, u0);
+                    u1 = fmaf(s[4 * m + 1], kk.y, u1);
+                    u0 = fmaf(s[4 * m + 2], kk.z, u0);
+                    u1 = fmaf(s[4 * m + 3], kk.w, u1);
+                    o0 = fmaf(s[4 * m + 0], qq.x, o0);
+                    o1 = fmaf(s[4 * m + 1], qq.y, o1);
+                    o0 = fmaf(s[4 * m + 2], qq.z, o0);
+                    o1 = fmaf(s[4 * m + 3], qq.w, o1);
+                }
+                const float u = group_sum<LPC>(u0 + u1); // S_old k (raw k)
+                const float o = group_sum<LPC>(o0 + o1); // S_old q (raw q)
+                const float a = g4.x, b = g4.y, rk = g4.z, rq = g4.w;
+                const float v = yt[2 * DK + col];
+                const float d = b * (v - (a * rk) * u); // b (v - a S_old k^)
+                const float dk = d * rk;                // S <- a S + d k^T, k^ = rk k
 #pragma unroll
-        for (int w = 0; w < W - 1; ++w)
-            cwin[k][w] = warm ? bf16_to_f32(win[int64_t(w) * p.C + c]) : 0.f;
+                for (int j = 0; j < KPL; ++j)
+                    s[j] = fmaf(dk, kr[j], a * s[j]);
+                if (jl == 0)
+                    ob[buf][tt][col] = fmaf(a * rq, o, kq * d); // a S_old q^ + d (k^.q^)
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int m = 0; m < KPL / 4; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                tile[(4 * jl + 4 * LPC * m + e) * DV + gcol] = s[4 * m + e];
+        return;
     }
 
-    for (int t0 = 0; t0 < L; t0 += CT) {
-        const int nt = min(CT, L - t0);
-        // A. stage raw inputs
-        for (int e = tid; e < nt * NCH; e += NT) {
-            const int tt = e / NCH, ch = e - tt * NCH;
-            ys[tt][ch] = bf16_to_f32(p.x[int64_t(tb + t0 + tt) * p.C + chan(ch)]);
+    // ========================= producer waves ===============================
+    const int pw = wave - NCONS;
+    const int plane = pw * 64 + lane;
+    const uint16_t* win = reinterpret_cast<const uint16_t*>(page + p.conv_off);
+
+    // conv taps and bias of the lane's channel pairs
+    float wq[Sh::NQK][2][W], wk[Sh::NQK][2][W], wv[Sh::NVS][2][W];
+    float bq[Sh::NQK][2], bk[Sh::NQK][2], bv[Sh::NVS][2];
+    auto load_taps = [&](int ch, float (&w2)[2][W], float (&b2)[2]) {
+        const int c = chan(ch);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int w = 0; w < W; ++w)
+                w2[i][w] = bf16_to_f32(p.conv_w[int64_t(c + i) * W + w]);
+            b2[i] = p.conv_b ? bf16_to_f32(p.conv_b[c + i]) : 0.f;
         }
-        if (tid < nt) {
-            s_a[tid] = p.alpha[int64_t(tb + t0 + tid) * p.Hv + h];
-            s_b[tid] = p.beta[int64_t(tb + t0 + tid) * p.Hv + h];
+    };
+#pragma unroll
+    for (int s = 0; s < Sh::NQK; ++s) {
+        const int pp = lane + 64 * s;
+        if (pp < QKP) {
+            load_taps(2 * pp, wq[s], bq[s]);
+            load_taps(DK + 2 * pp, wk[s], bk[s]);
         }
-        __syncthreads();
-        // B. conv + SiLU
+    }
 #pragma unroll
-        for (int k = 0; k < Sh::CPT; ++k) {
-            const int ch = tid + k * NT;
-            if (ch < NCH) {
-                for (int tt = 0; tt < nt; ++tt) {
-                    const float xv = ys[tt][ch];
-                    float acc = cb[k];
+    for (int s = 0; s < Sh::NVS; ++s) {
+        const int pp = lane + 64 * s;
+        if (pp < Sh::NVP)
+            load_taps(2 * DK + 2 * pp, wv[s], bv[s]);
+    }
+
+    // chunk k's raw rows and gates: issue (into registers), then stage (to LDS)
+    uint4 pf[Sh::LOADS];
+    float2 pg = make_float2(0.f, 0.f);
+    auto issue = [&](int k) {
+        if (k >= nchunks)
+            return;
+        const int nt = chunk_len(k);
 #pragma unroll
-                    for (int w = 0; w < W - 1; ++w)
-                        acc += cw[k][w] * cwin[k][w];
-                    acc += cw[k][W - 1] * xv;
-#pragma unroll
-                    for (int w = 0; w + 1 < W - 1; ++w)
-                        cwin[k][w] = cwin[k][w + 1];
-                    cwin[k][W - 2] = xv;
-                    ys[tt][ch] = silu(acc);
+        for (int i = 0; i < Sh::LOADS; ++i) {
+            const int e = plane + PLANES * i;
+            if (e < nt * NPIECE) {
+                const int tt = e / NPIECE, pc = e - tt * NPIECE;
+                const uint16_t* src = p.x + int64_t(tb + k * CT + tt) * p.C + chan(8 * pc);
+                if (p.x_vec) {
+                    pf[i] = *reinterpret_cast<const uint4*>(src);
+                } else {
+                    const uint32_t* s4 = reinterpret_cast<const uint32_t*>(src);
+                    pf[i] = make_uint4(s4[0], s4[1], s4[2], s4[3]);
                 }
             }
         }
-        __syncthreads();
-        // C. norms, one wave per token
-        for (int tt = wave; tt < nt; tt += Sh::NWP) {
+        if (plane < nt) {
+            const int64_t gi = int64_t(tb + k * CT + plane) * p.Hv + h;
+            pg = make_float2(p.alpha[gi], p.beta[gi]);
+        }
+    };
+    auto stage = [&](int k) {
+        if (k >= nchunks)
+            return;
+        const int nt = chunk_len(k);
+#pragma unroll
+        for (int i = 0; i < Sh::LOADS; ++i) {
+            const int e = plane + PLANES * i;
+            if (e < nt * NPIECE) {
+                const int tt = e / NPIECE, pc = e - tt * NPIECE;
+                *reinterpret_cast<uint4*>(&raw[ring_pos<RING>(k * CT + tt)][8 * pc]) = pf[i];
+            }
+        }
+        if (plane < nt)
+            *reinterpret_cast<float2*>(gab[ring_pos<RING>(k * CT + plane)]) = pg;
+    };
+
+    // conv + SiLU and the norm factors of chunk k into ys[k & 1], sc[k & 1]
+    auto prepare = [&](int k) {
+        const int buf = k & 1;
+        const int nt = chunk_len(k);
+        for (int tt = pw; tt < nt; tt += Sh::NPROD) {
+            const int tok = k * CT + tt;
+            const uint32_t* rows[W];
+#pragma unroll
+            for (int w = 0; w < W; ++w)
+                rows[w] = reinterpret_cast<const uint32_t*>(raw[ring_pos<RING>(tok - (W - 1) + w)]);
             float sq = 0.f, sk = 0.f, qk = 0.f;
-            for (int j = lane; j < DK; j += 64) {
-                const float a = ys[tt][j], b = ys[tt][DK + j];
-                sq += a * a;
-                sk += b * b;
-                qk += a * b;
+#pragma unroll
+            for (int s = 0; s < Sh::NQK; ++s) {
+                const int pp = lane + 64 * s;
+                if (pp < QKP) {
+                    float q0 = bq[s][0], q1 = bq[s][1], k0 = bk[s][0], k1 = bk[s][1];
+#pragma unroll
+                    for (int w = 0; w < W; ++w) {
+                        const uint32_t xq = rows[w][pp], xk = rows[w][QKP + pp];
+                        q0 = fmaf(wq[s][0][w], lo_bf16(xq), q0);
+                        q1 = fmaf(wq[s][1][w], hi_bf16(xq), q1);
+                        k0 = fmaf(wk[s][0][w], lo_bf16(xk), k0);
+                        k1 = fmaf(wk[s][1][w], hi_bf16(xk), k1);
+                    }
+                    q0 = silu(q0);
+                    q1 = silu(q1);
+                    k0 = silu(k0);
+                    k1 = silu(k1);
+                    *reinterpret_cast<float2*>(&ys[buf][tt][2 * pp]) = make_float2(q0, q1);
+                    *reinterpret_cast<float2*>(&ys[buf][tt][DK + 2 * pp]) = make_float2(k0, k1);
+                    sq = fmaf(q0, q0, fmaf(q1, q1, sq));
+                    sk = fmaf(k0, k0, fmaf(k1, k1, sk));
+                    qk = fmaf(q0, k0, fmaf(q1, k1, qk));
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < Sh::NVS; ++s) {
+                const int pp = lane + 64 * s;
+                if (pp < Sh::NVP) {
+                    float v0 = bv[s][0], v1 = bv[s][1];
+#pragma unroll
+                    for (int w = 0; w < W; ++w) {
+                        const uint32_t xv = rows[w][2 * QKP + pp];
+                        v0 = fmaf(wv[s][0][w], lo_bf16(xv), v0);
+                        v1 = fmaf(wv[s][1][w], hi_bf16(xv), v1);
+                    }
+                    *reinterpret_cast<float2*>(&ys[buf][tt][2 * DK + 2 * pp]) =
+                        make_float2(silu(v0), silu(v1));
+                }
             }
             sq = group_sum<64>(sq);
             sk = group_sum<64>(sk);
             qk = group_sum<64>(qk);
-            const float rq = p.scale / sqrtf(sq + p.eps);
-            const float rk = 1.0f / sqrtf(sk + p.eps);
-            for (int j = lane; j < DK; j += 64) {
-                ys[tt][j] *= rq;
-                ys[tt][DK + j] *= rk;
-            }
-            if (lane == 0)
-                s_kq[tt] = qk * rq * rk;
-        }
-        __syncthreads();
-        // D. recurrence
-        for (int tt = 0; tt < nt; ++tt) {
-            float kh[JPL], qh[JPL];
-#pragma unroll
-            for (int m = 0; m < JPL; ++m) {
-                qh[m] = ys[tt][jl + LPC * m];
-                kh[m] = ys[tt][DK + jl + LPC * m];
-            }
-            const float4 v = *reinterpret_cast<const float4*>(&ys[tt][2 * DK + il]);
-            const float a = s_a[tt], b = s_b[tt], kq = s_kq[tt];
-            float4 u = make_float4(0.f, 0.f, 0.f, 0.f), o = u;
-#pragma unroll
-            for (int m = 0; m < JPL; ++m) {
-                u.x += s[m].x * kh[m];
-                u.y += s[m].y * kh[m];
-                u.z += s[m].z * kh[m];
-                u.w += s[m].w * kh[m];
-                o.x += s[m].x * qh[m];
-                o.y += s[m].y * qh[m];
-                o.z += s[m].z * qh[m];
-                o.w += s[m].w * qh[m];
-            }
-            u.x = group_sum<LPC>(u.x);
-            u.y = group_sum<LPC>(u.y);
-            u.z = group_sum<LPC>(u.z);
-            u.w = group_sum<LPC>(u.w);
-            o.x = group_sum<LPC>(o.x);
-            o.y = group_sum<LPC>(o.y);
-            o.z = group_sum<LPC>(o.z);
-            o.w = group_sum<LPC>(o.w);
-            float4 d;
-            d.x = b * (v.x - a * u.x);
-            d.y = b * (v.y - a * u.y);
-            d.z = b * (v.z - a * u.z);
-            d.w = b * (v.w - a * u.w);
-#pragma unroll
-            for (int m = 0; m < JPL; ++m) {
-                s[m].x = fmaf(d.x, kh[m], a * s[m].x);
-                s[m].y = fmaf(d.y, kh[m], a * s[m].y);
-                s[m].z = fmaf(d.z, kh[m], a * s[m].z);
-                s[m].w = fmaf(d.w, kh[m], a * s[m].w);
-            }
-            if (jl == 0) {
-                *reinterpret_cast<uint2*>(out + int64_t(t0 + tt) * out_stride) =
-                    pack_bf16x4(fmaf(d.x, kq, a * o.x), fmaf(d.y, kq, a * o.y),
-                                fmaf(d.z, kq, a * o.z), fmaf(d.w, kq, a * o.w));
+            if (lane == 0) {
+                const float rq = p.scale / sqrtf(sq + p.eps);
+                const float rk = 1.0f / sqrtf(sk + p.eps);
+                const float2 ab = *reinterpret_cast<const float2*>(gab[ring_pos<RING>(tok)]);
+                *reinterpret_cast<float4*>(sc[buf][tt]) = make_float4(ab.x, ab.y, rk, rq);
+                sc[buf][tt][4] = qk * rq * rk;
             }
         }
+    };
+
+    // chunk k's outputs from ob[k & 1] to HBM as bf16
+    auto flush = [&](int k) {
+        const int buf = k & 1;
+        const int nt = chunk_len(k);
+        for (int e = plane; e < nt * Sh::OPR; e += PLANES) {
+            const int tt = e / Sh::OPR, c8 = e - tt * Sh::OPR;
+            const float4 lo = *reinterpret_cast<const float4*>(&ob[buf][tt][8 * c8]);
+            const float4 hi = *reinterpret_cast<const float4*>(&ob[buf][tt][8 * c8 + 4]);
+            const uint2 a = pack_bf16x4(lo.x, lo.y, lo.z, lo.w);
+            const uint2 b = pack_bf16x4(hi.x, hi.y, hi.z, hi.w);
+            uint16_t* dst = out_base + int64_t(k * CT + tt) * out_tok + 8 * c8;
+            if (p.out_vec) {
+                *reinterpret_cast<uint4*>(dst) = make_uint4(a.x, a.y, b.x, b.y);
+            } else {
+                reinterpret_cast<uint2*>(dst)[0] = a;
+                reinterpret_cast<uint2*>(dst)[1] = b;
+            }
+        }
+    };
+
+    // prologue: the W-1 inputs before the first token (window or zeros), chunk 0
+    for (int e = plane; e < (W - 1) * NCH; e += PLANES) {
+        const int w = e / NCH, ch = e - w * NCH;
+        raw[ring_pos<RING>(w - (W - 1))][ch] = warm ? win[int64_t(w) * p.C + chan(ch)] : uint16_t(0);
+    }
+    issue(0);
+    stage(0);
+    __syncthreads(); // A
+    issue(1);
+    prepare(0);
+    stage(1);
+    __syncthreads(); // B
+    for (int c = 0; c < nchunks; ++c) {
+        issue(c + 2);
+        if (c + 1 < nchunks)
+            prepare(c + 1);
+        if (c >= 1)
+            flush(c - 1);
+        stage(c + 2);
         __syncthreads();
     }
-
-#pragma unroll
-    for (int m = 0; m < JPL; ++m)
-        *reinterpret_cast<float4*>(tile + (jl + LPC * m) * DV + i0) = s[m];
+    flush(nchunks - 1);
 }
 
 // Final window of each sequence: the last W-1 entries of (old window, x).
@@ -317,6 +466,8 @@ int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, cons
     p.C = d.conv_channels;
     p.Hk = d.num_k_heads;
     p.Hv = d.num_v_heads;
+    p.x_vec = (reinterpret_cast<uintptr_t>(a->x) & 15u) == 0;
+    p.out_vec = (reinterpret_cast<uintptr_t>(a->out) & 15u) == 0;
     p.cu = cu;
     p.x = a->x;
     p.conv_w = a->conv_w;

@@ -73,6 +73,23 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+// Sum over the whole wavefront as a wave-uniform value: sums within each row
+// of 16 lanes, then rows 1 and 3 add the last lane of rows 0 and 2, then rows
+// 2 and 3 add lane 31; lane 63 then holds the total and is read out.  Only
+// DPP moves, no LDS permutes.
+__device__ __forceinline__ float wave_total(float v)
+{
+    v = group_sum<16>(v);
+    v += __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast15, 0xA, 0xF, false));
+    v += __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast31, 0xC, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Hardware dispatches workgroup b to XCD b % 8.  Renumber so that each XCD
 // receives a contiguous run of logical ids (neighbours share its L2).
 __device__ __forceinline__ int xcd_contiguous_id(int b, int nblocks)

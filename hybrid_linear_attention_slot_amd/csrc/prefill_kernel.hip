@@ -49,7 +49,7 @@ struct PrefillShape {
     static constexpr int LPC = DK / KPL;                            // lanes sharing one column
     static constexpr int CPW = 64 / LPC;                            // columns per consumer wave
     static constexpr int NCONS = (DV / CPW) < 4 ? (DV / CPW) : 4;   // consumer waves
-    static constexpr int NPROD = 2;                                 // producer waves
+    static constexpr int NPROD = 4;                                 // producer waves
     static constexpr int ISZ = NCONS * CPW;                         // value columns per workgroup
     static constexpr int NSL = DV / ISZ;                            // workgroups per head
     static constexpr int NT = 64 * (NCONS + NPROD);
@@ -64,6 +64,7 @@ struct PrefillShape {
     static constexpr int PLANES = 64 * NPROD;
     static constexpr int LOADS = (CT * NPIECE + PLANES - 1) / PLANES; // pieces per producer lane
     static constexpr int OPR = ISZ / 8;                             // 8-column output pieces per row
+    static constexpr int TPW = CT / NPROD;                          // tokens per producer wave
     static_assert(DK == DV, "square heads only");
     static_assert(KPL % 4 == 0 && DK % KPL == 0 && LPC >= 1 && LPC <= 64, "key split");
     static_assert(NCONS >= 1 && DV % ISZ == 0 && ISZ % 8 == 0, "column split");
@@ -79,8 +80,6 @@ struct PrefillParams {
     int32_t C;
     int32_t Hk;
     int32_t Hv;
-    int32_t x_vec;   // x is 16-byte aligned
-    int32_t out_vec; // out is 16-byte aligned
     const int32_t* cu;
     const uint16_t* x;
     const uint16_t* conv_w;
@@ -131,7 +130,8 @@ __global__ __launch_bounds__((PrefillShape<DK, DV>::NT)) void prefill_kernel(Pre
     const int sl = r1 % Sh::NSL;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform: role and token
+    const int lane = tid & 63;                                 // indices go to scalar registers
     const int tb = p.cu[n];
     const int L = p.cu[n + 1] - tb;
     if (L <= 0)
@@ -172,45 +172,75 @@ __global__ __launch_bounds__((PrefillShape<DK, DV>::NT)) void prefill_kernel(Pre
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 s[4 * m + e] = warm ? tile[(4 * jl + 4 * LPC * m + e) * DV + gcol] : 0.f;
+        // operands of one token; the next token's are fetched from LDS while
+        // the current one is computed
+        struct Ops {
+            float4 k[KPL / 4], q[KPL / 4];
+            float4 g; // a, b, rk, rq
+            float kq, v;
+        };
+        auto fetch = [&](Ops& r, int buf, int tt) {
+            const float* yt = ys[buf][tt];
+#pragma unroll
+            for (int m = 0; m < KPL / 4; ++m) {
+                r.k[m] = *reinterpret_cast<const float4*>(yt + DK + 4 * jl + 4 * LPC * m);
+                r.q[m] = *reinterpret_cast<const float4*>(yt + 4 * jl + 4 * LPC * m);
+            }
+            r.g = *reinterpret_cast<const float4*>(sc[buf][tt]);
+            r.kq = sc[buf][tt][4];
+            r.v = yt[2 * DK + col];
+        };
+        auto step = [&](const Ops& r, int buf, int tt) {
+            float u0 = 0.f, u1 = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+            for (int m = 0; m < KPL / 4; ++m) {
+                u0 = fmaf(s[4 * m + 0], r.k[m].x, u0);
+                u1 = fmaf(s[4 * m + 1], r.k[m].y, u1);
+                o0 = fmaf(s[4 * m + 0], r.q[m].x, o0);
+                o1 = fmaf(s[4 * m + 1], r.q[m].y, o1);
+                u0 = fmaf(s[4 * m + 2], r.k[m].z, u0);
+                u1 = fmaf(s[4 * m + 3], r.k[m].w, u1);
+                o0 = fmaf(s[4 * m + 2], r.q[m].z, o0);
+                o1 = fmaf(s[4 * m + 3], r.q[m].w, o1);
+            }
+            const float u = group_sum<LPC>(u0 + u1); // S_old k (raw k)
+            const float o = group_sum<LPC>(o0 + o1); // S_old q (raw q)
+            const float a = r.g.x, b = r.g.y, rk = r.g.z, rq = r.g.w;
+            const float d = b * (r.v - (a * rk) * u); // b (v - a S_old k^)
+            const float dk = d * rk;                  // S <- a S + d k^T, k^ = rk k
+#pragma unroll
+            for (int m = 0; m < KPL / 4; ++m) {
+                s[4 * m + 0] = fmaf(dk, r.k[m].x, a * s[4 * m + 0]);
+                s[4 * m + 1] = fmaf(dk, r.k[m].y, a * s[4 * m + 1]);
+                s[4 * m + 2] = fmaf(dk, r.k[m].z, a * s[4 * m + 2]);
+                s[4 * m + 3] = fmaf(dk, r.k[m].w, a * s[4 * m + 3]);
+            }
+            const float ov = fmaf(a * rq, o, r.kq * d); // a S_old q^ + d (k^.q^)
+            if (jl == 0)
+                ob[buf][tt][col] = ov;
+        };
         __syncthreads(); // A: history and chunk 0 staged
         __syncthreads(); // B: chunk 0 prepared
         for (int c = 0; c < nchunks; ++c) {
             const int buf = c & 1;
             const int nt = chunk_len(c);
-            for (int tt = 0; tt < nt; ++tt) {
-                const float* yt = ys[buf][tt];
-                const float4 g4 = *reinterpret_cast<const float4*>(sc[buf][tt]);
-                const float kq = sc[buf][tt][4];
-                float kr[KPL];
-                float u0 = 0.f, u1 = 0.f, o0 = 0.f, o1 = 0.f;
-#pragma unroll
-                for (int m = 0; m < KPL / 4; ++m) {
-                    const float4 kk = *reinterpret_cast<const float4*>(yt + DK + 4 * jl + 4 * LPC * m);
-                    const float4 qq = *reinterpret_cast<const float4*>(yt + 4 * jl + 4 * LPC * m);
-                    kr[4 * m + 0] = kk.x;
-                    kr[4 * m + 1] = kk.y;
-                    kr[4 * m + 2] = kk.z;
-                    kr[4 * m + 3] = kk.w;
-                    u0 = fmaf(s[4 * m + 0], kk.x, u0);
-                    u1 = fmaf(s[4 * m + 1], kk.y, u1);
-                    u0 = fmaf(s[4 * m + 2], kk.z, u0);
-                    u1 = fmaf(s[4 * m + 3], kk.w, u1);
-                    o0 = fmaf(s[4 * m + 0], qq.x, o0);
-                    o1 = fmaf(s[4 * m + 1], qq.y, o1);
-                    o0 = fmaf(s[4 * m + 2], qq.z, o0);
-                    o1 = fmaf(s[4 * m + 3], qq.w, o1);
+            Ops A, B;
+            if (nt == CT) {
+                // full chunk: a fixed-trip loop without branches, so that each
+                // token waits only for its own operands (the last fetch of the
+                // chunk re-reads token CT-1 and is unused)
+                fetch(A, buf, 0);
+                for (int tt = 0; tt < CT; tt += 2) {
+                    fetch(B, buf, tt + 1);
+                    step(A, buf, tt);
+                    fetch(A, buf, min(tt + 2, CT - 1));
+                    step(B, buf, tt + 1);
                 }
-                const float u = group_sum<LPC>(u0 + u1); // S_old k (raw k)
-                const float o = group_sum<LPC>(o0 + o1); // S_old q (raw q)
-                const float a = g4.x, b = g4.y, rk = g4.z, rq = g4.w;
-                const float v = yt[2 * DK + col];
-                const float d = b * (v - (a * rk) * u); // b (v - a S_old k^)
-                const float dk = d * rk;                // S <- a S + d k^T, k^ = rk k
-#pragma unroll
-                for (int j = 0; j < KPL; ++j)
-                    s[j] = fmaf(dk, kr[j], a * s[j]);
-                if (jl == 0)
-                    ob[buf][tt][col] = fmaf(a * rq, o, kq * d); // a S_old q^ + d (k^.q^)
+            } else {
+                for (int tt = 0; tt < nt; ++tt) {
+                    fetch(A, buf, tt);
+                    step(A, buf, tt);
+                }
             }
             __syncthreads();
         }
@@ -255,108 +285,149 @@ __global__ __launch_bounds__((PrefillShape<DK, DV>::NT)) void prefill_kernel(Pre
             load_taps(2 * DK + 2 * pp, wv[s], bv[s]);
     }
 
-    // chunk k's raw rows and gates: issue (into registers), then stage (to LDS)
+    // chunk k's raw rows and gates: issue (into registers), then stage (to LDS).
+    // Every lane issues the same number of 16-byte loads whatever the chunk's
+    // length (pieces past the last token re-read the last token's row and land
+    // in ring rows no conv reads), so the waits for them are exact.
     uint4 pf[Sh::LOADS];
-    float2 pg = make_float2(0.f, 0.f);
+    float2 pg;
     auto issue = [&](int k) {
         if (k >= nchunks)
             return;
-        const int nt = chunk_len(k);
+        const int last = chunk_len(k) - 1;
 #pragma unroll
         for (int i = 0; i < Sh::LOADS; ++i) {
-            const int e = plane + PLANES * i;
-            if (e < nt * NPIECE) {
-                const int tt = e / NPIECE, pc = e - tt * NPIECE;
-                const uint16_t* src = p.x + int64_t(tb + k * CT + tt) * p.C + chan(8 * pc);
-                if (p.x_vec) {
-                    pf[i] = *reinterpret_cast<const uint4*>(src);
-                } else {
-                    const uint32_t* s4 = reinterpret_cast<const uint32_t*>(src);
-                    pf[i] = make_uint4(s4[0], s4[1], s4[2], s4[3]);
-                }
-            }
+            const int e = min(plane + PLANES * i, CT * NPIECE - 1);
+            const int tt = e / NPIECE, pc = e - tt * NPIECE;
+            pf[i] = *reinterpret_cast<const uint4*>(p.x + int64_t(tb + k * CT + min(tt, last)) * p.C +
+                                                   chan(8 * pc));
         }
-        if (plane < nt) {
-            const int64_t gi = int64_t(tb + k * CT + plane) * p.Hv + h;
-            pg = make_float2(p.alpha[gi], p.beta[gi]);
-        }
+        const int64_t gi = int64_t(tb + k * CT + min(plane % CT, last)) * p.Hv + h;
+        pg = make_float2(p.alpha[gi], p.beta[gi]);
     };
     auto stage = [&](int k) {
         if (k >= nchunks)
             return;
-        const int nt = chunk_len(k);
 #pragma unroll
         for (int i = 0; i < Sh::LOADS; ++i) {
             const int e = plane + PLANES * i;
-            if (e < nt * NPIECE) {
+            if (e < CT * NPIECE) {
                 const int tt = e / NPIECE, pc = e - tt * NPIECE;
                 *reinterpret_cast<uint4*>(&raw[ring_pos<RING>(k * CT + tt)][8 * pc]) = pf[i];
             }
         }
-        if (plane < nt)
+        if (plane < CT)
             *reinterpret_cast<float2*>(gab[ring_pos<RING>(k * CT + plane)]) = pg;
     };
 
-    // conv + SiLU and the norm factors of chunk k into ys[k & 1], sc[k & 1]
+    // conv + SiLU and the norm factors of chunk k into ys[k & 1], sc[k & 1].
+    // Producer wave pw takes the TPW consecutive tokens starting at pw * TPW;
+    // each lane walks them in order for its channel pairs, keeping the W-1
+    // previous inputs of each channel in registers (primed from the ring), so
+    // every staged input is unpacked once.  The wave sums of |q|^2, |k|^2 and
+    // q.k of the tokens are formed together at the end, and lane i finishes
+    // the norm factors of the wave's i-th token.
     auto prepare = [&](int k) {
+        constexpr int TPW = Sh::TPW;
         const int buf = k & 1;
-        const int nt = chunk_len(k);
-        for (int tt = pw; tt < nt; tt += Sh::NPROD) {
-            const int tok = k * CT + tt;
-            const uint32_t* rows[W];
+        const int t0 = pw * TPW;
+        const int t1 = min(t0 + TPW, chunk_len(k));
+        if (t0 >= t1)
+            return;
+        const int base = (k % 3) * CT; // ring row of the chunk's first token
+        auto row = [&](int tt) {       // tt in [-(W-1), CT)
+            const int r = base + tt;
+            return reinterpret_cast<const uint32_t*>(raw[r < 0 ? r + RING : r]);
+        };
+        float hq[Sh::NQK][2][W - 1], hk[Sh::NQK][2][W - 1], hv[Sh::NVS][2][W - 1];
 #pragma unroll
-            for (int w = 0; w < W; ++w)
-                rows[w] = reinterpret_cast<const uint32_t*>(raw[ring_pos<RING>(tok - (W - 1) + w)]);
-            float sq = 0.f, sk = 0.f, qk = 0.f;
+        for (int w = 0; w < W - 1; ++w) {
+            const uint32_t* r = row(t0 - (W - 1) + w);
+#pragma unroll
+            for (int s = 0; s < Sh::NQK; ++s) {
+                const int pp = min(lane + 64 * s, QKP - 1);
+                const uint32_t xq = r[pp], xk = r[QKP + pp];
+                hq[s][0][w] = lo_bf16(xq);
+                hq[s][1][w] = hi_bf16(xq);
+                hk[s][0][w] = lo_bf16(xk);
+                hk[s][1][w] = hi_bf16(xk);
+            }
+#pragma unroll
+            for (int s = 0; s < Sh::NVS; ++s) {
+                const uint32_t xv = r[2 * QKP + min(lane + 64 * s, Sh::NVP - 1)];
+                hv[s][0][w] = lo_bf16(xv);
+                hv[s][1][w] = hi_bf16(xv);
+            }
+        }
+        // conv of one channel: taps over the W-1 held inputs and the current one,
+        // then the held inputs shift by one
+        auto conv1 = [&](const float (&wt)[W], float b, float (&hist)[W - 1], float x) {
+            float acc = b;
+#pragma unroll
+            for (int w = 0; w < W - 1; ++w)
+                acc = fmaf(wt[w], hist[w], acc);
+            acc = fmaf(wt[W - 1], x, acc);
+#pragma unroll
+            for (int w = 0; w + 1 < W - 1; ++w)
+                hist[w] = hist[w + 1];
+            hist[W - 2] = x;
+            return silu(acc);
+        };
+        float sq[TPW], sk[TPW], qk[TPW];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            sq[i] = sk[i] = qk[i] = 0.f;
+            const int tt = t0 + i;
+            if (tt >= t1)
+                break;
+            const uint32_t* r = row(tt);
+            float* yt = ys[buf][tt];
 #pragma unroll
             for (int s = 0; s < Sh::NQK; ++s) {
                 const int pp = lane + 64 * s;
+                const int pc = min(pp, QKP - 1);
+                const uint32_t xq = r[pc], xk = r[QKP + pc];
+                const float q0 = conv1(wq[s][0], bq[s][0], hq[s][0], lo_bf16(xq));
+                const float q1 = conv1(wq[s][1], bq[s][1], hq[s][1], hi_bf16(xq));
+                const float k0 = conv1(wk[s][0], bk[s][0], hk[s][0], lo_bf16(xk));
+                const float k1 = conv1(wk[s][1], bk[s][1], hk[s][1], hi_bf16(xk));
                 if (pp < QKP) {
-                    float q0 = bq[s][0], q1 = bq[s][1], k0 = bk[s][0], k1 = bk[s][1];
-#pragma unroll
-                    for (int w = 0; w < W; ++w) {
-                        const uint32_t xq = rows[w][pp], xk = rows[w][QKP + pp];
-                        q0 = fmaf(wq[s][0][w], lo_bf16(xq), q0);
-                        q1 = fmaf(wq[s][1][w], hi_bf16(xq), q1);
-                        k0 = fmaf(wk[s][0][w], lo_bf16(xk), k0);
-                        k1 = fmaf(wk[s][1][w], hi_bf16(xk), k1);
-                    }
-                    q0 = silu(q0);
-                    q1 = silu(q1);
-                    k0 = silu(k0);
-                    k1 = silu(k1);
-                    *reinterpret_cast<float2*>(&ys[buf][tt][2 * pp]) = make_float2(q0, q1);
-                    *reinterpret_cast<float2*>(&ys[buf][tt][DK + 2 * pp]) = make_float2(k0, k1);
-                    sq = fmaf(q0, q0, fmaf(q1, q1, sq));
-                    sk = fmaf(k0, k0, fmaf(k1, k1, sk));
-                    qk = fmaf(q0, k0, fmaf(q1, k1, qk));
+                    *reinterpret_cast<float2*>(yt + 2 * pp) = make_float2(q0, q1);
+                    *reinterpret_cast<float2*>(yt + DK + 2 * pp) = make_float2(k0, k1);
+                    sq[i] = fmaf(q0, q0, q1 * q1);
+                    sk[i] = fmaf(k0, k0, k1 * k1);
+                    qk[i] = fmaf(q0, k0, q1 * k1);
                 }
             }
 #pragma unroll
             for (int s = 0; s < Sh::NVS; ++s) {
                 const int pp = lane + 64 * s;
-                if (pp < Sh::NVP) {
-                    float v0 = bv[s][0], v1 = bv[s][1];
+                const uint32_t xv = r[2 * QKP + min(pp, Sh::NVP - 1)];
+                const float v0 = conv1(wv[s][0], bv[s][0], hv[s][0], lo_bf16(xv));
+                const float v1 = conv1(wv[s][1], bv[s][1], hv[s][1], hi_bf16(xv));
+                if (pp < Sh::NVP)
+                    *reinterpret_cast<float2*>(yt + 2 * DK + 2 * pp) = make_float2(v0, v1);
+            }
+        }
+        float my_sq = 0.f, my_sk = 0.f, my_qk = 0.f;
 #pragma unroll
-                    for (int w = 0; w < W; ++w) {
-                        const uint32_t xv = rows[w][2 * QKP + pp];
-                        v0 = fmaf(wv[s][0][w], lo_bf16(xv), v0);
-                        v1 = fmaf(wv[s][1][w], hi_bf16(xv), v1);
-                    }
-                    *reinterpret_cast<float2*>(&ys[buf][tt][2 * DK + 2 * pp]) =
-                        make_float2(silu(v0), silu(v1));
-                }
+        for (int i = 0; i < TPW; ++i) {
+            if (t0 + i >= t1)
+                break;
+            const float tq = wave_total(sq[i]), tk = wave_total(sk[i]), tx = wave_total(qk[i]);
+            if (lane == i) {
+                my_sq = tq;
+                my_sk = tk;
+                my_qk = tx;
             }
-            sq = group_sum<64>(sq);
-            sk = group_sum<64>(sk);
-            qk = group_sum<64>(qk);
-            if (lane == 0) {
-                const float rq = p.scale / sqrtf(sq + p.eps);
-                const float rk = 1.0f / sqrtf(sk + p.eps);
-                const float2 ab = *reinterpret_cast<const float2*>(gab[ring_pos<RING>(tok)]);
-                *reinterpret_cast<float4*>(sc[buf][tt]) = make_float4(ab.x, ab.y, rk, rq);
-                sc[buf][tt][4] = qk * rq * rk;
-            }
+        }
+        const int tt = t0 + lane;
+        if (lane < TPW && tt < t1) {
+            const float rq = p.scale / sqrtf(my_sq + p.eps);
+            const float rk = 1.0f / sqrtf(my_sk + p.eps);
+            const float2 ab = *reinterpret_cast<const float2*>(gab[base + tt]);
+            *reinterpret_cast<float4*>(sc[buf][tt]) = make_float4(ab.x, ab.y, rk, rq);
+            sc[buf][tt][4] = my_qk * rq * rk;
         }
     };
 
@@ -370,13 +441,8 @@ __global__ __launch_bounds__((PrefillShape<DK, DV>::NT)) void prefill_kernel(Pre
             const float4 hi = *reinterpret_cast<const float4*>(&ob[buf][tt][8 * c8 + 4]);
             const uint2 a = pack_bf16x4(lo.x, lo.y, lo.z, lo.w);
             const uint2 b = pack_bf16x4(hi.x, hi.y, hi.z, hi.w);
-            uint16_t* dst = out_base + int64_t(k * CT + tt) * out_tok + 8 * c8;
-            if (p.out_vec) {
-                *reinterpret_cast<uint4*>(dst) = make_uint4(a.x, a.y, b.x, b.y);
-            } else {
-                reinterpret_cast<uint2*>(dst)[0] = a;
-                reinterpret_cast<uint2*>(dst)[1] = b;
-            }
+            *reinterpret_cast<uint4*>(out_base + int64_t(k * CT + tt) * out_tok + 8 * c8) =
+                make_uint4(a.x, a.y, b.x, b.y);
         }
     };
 
@@ -393,12 +459,14 @@ __global__ __launch_bounds__((PrefillShape<DK, DV>::NT)) void prefill_kernel(Pre
     stage(1);
     __syncthreads(); // B
     for (int c = 0; c < nchunks; ++c) {
+        // the loads are consumed by stage() after prepare(); the output stores
+        // go last, so that no wait for loads also waits for fresh stores
         issue(c + 2);
         if (c + 1 < nchunks)
             prepare(c + 1);
+        stage(c + 2);
         if (c >= 1)
             flush(c - 1);
-        stage(c + 2);
         __syncthreads();
     }
     flush(nchunks - 1);
@@ -466,8 +534,6 @@ int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, cons
     p.C = d.conv_channels;
     p.Hk = d.num_k_heads;
     p.Hv = d.num_v_heads;
-    p.x_vec = (reinterpret_cast<uintptr_t>(a->x) & 15u) == 0;
-    p.out_vec = (reinterpret_cast<uintptr_t>(a->out) & 15u) == 0;
     p.cu = cu;
     p.x = a->x;
     p.conv_w = a->conv_w;

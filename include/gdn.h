@@ -177,6 +177,7 @@ typedef struct {
  * window and state are taken as zero and the page is not read.  The updated
  * window and state are written back into the same page.  All pointers in
  * `args` are device pointers (conv_b may be NULL).  rows == 0 is a no-op.
+ * Alignment: x, conv_w and conv_b 4-byte aligned, out 8-byte aligned.
  * Errors: GDN_EINVAL (NULL pointer, rows < 0), GDN_ERANGE (layer out of
  * range or attention-only), GDN_EUNSUPPORTED (head dims), GDN_EALIGN. */
 int gdn_decode_step(const gdn_pool* pool, int32_t layer, int32_t rows,
@@ -188,7 +189,9 @@ int gdn_decode_step(const gdn_pool* pool, int32_t layer, int32_t rows,
  * cu_seqlens_dev: device int32 [num_seqs + 1], non-decreasing, cu[0] == 0,
  * cu[num_seqs] == total_tokens (not checkable on the host).  max_seqlen is an
  * upper bound of the lengths (host hint).  A zero-length sequence leaves its
- * slot untouched.  Errors as for gdn_decode_step. */
+ * slot untouched.  Alignment: x and out 16-byte aligned (the inputs are read
+ * and the outputs written in 16-byte pieces), conv_w and conv_b 4-byte
+ * aligned.  Errors as for gdn_decode_step. */
 int gdn_prefill_varlen(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
                        const int32_t* cu_seqlens_dev, int32_t max_seqlen, int64_t total_tokens,
                        const gdn_step_args* args, gdn_stream_t stream);

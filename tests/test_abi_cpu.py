@@ -138,6 +138,10 @@ def test_step_validation():
     with pytest.raises(gdn.GdnError) as e:
         gdn.gdn_decode_step(p, 0, 4, step_args(conv_w=FAKE + 2), stream=0)
     assert e.value.code == gdn.GDN_EALIGN
+    for over in (dict(x=FAKE + 8), dict(out=FAKE + 8)):
+        with pytest.raises(gdn.GdnError) as e:
+            gdn.gdn_prefill_varlen(p, 0, 2, FAKE, 8, 16, step_args(**over), stream=0)
+        assert e.value.code == gdn.GDN_EALIGN
     # zero rows / zero tokens are no-ops that launch nothing
     assert gdn.gdn_decode_step(p, 0, 0, a, stream=0) == gdn.GDN_OK
     assert gdn.gdn_prefill_varlen(p, 0, 0, FAKE, 0, 0, a, stream=0) == gdn.GDN_OK

@@ -17,16 +17,19 @@
 //     workgroups touch the same window channels, and q/k are computed once.
 //   - each v-head's dk x dv fp32 state tile is streamed once from HBM into
 //     registers and once back.  The tile is stored key-major ([dk][dv], value
-//     index contiguous).  A lane holds four consecutive value columns (one
-//     float4) for JPL keys; the LPC lanes that share a float4 column split
-//     the keys between them.  With dk = dv = 128: 4 waves, 8 columns of 16 B
-//     per key row per load instruction (8 full 128-byte lines), 16 float4 per
-//     lane.
-//   - S k and S q are lane-partial dot products over the lane's keys followed
-//     by a DPP sum over the LPC lanes; o is formed without a second pass over
-//     S:  o = a (S_old q) + d (k.q)  with  d = b (v - a S_old k).
-//   - the state loads of the first head are issued before the conv so that
-//     the conv and the norms overlap them.
+//     index contiguous).  Wave w owns the key rows [w KPW, (w+1) KPW) of every
+//     tile and walks them RPI rows (1 KiB with dv = 128) per load or store
+//     instruction, each lane holding one float4 of value columns; a wave's
+//     consecutive memory instructions therefore touch consecutive kilobytes,
+//     the order in which the HBM stream of this in-place read-modify-write
+//     runs fastest.
+//   - S k and S q are lane-partial dot products over the lane's key rows,
+//     summed over the RPI lanes of a column with cross-lane moves and over
+//     the waves through LDS (one barrier for both heads of a pair, fixed
+//     summation order); o is formed without a second pass over S:
+//     o = a (S_old q) + d (k.q)  with  d = b (v - a S_old k).
+//   - the state loads of the first two heads are issued before the conv so
+//     that the conv and the norms overlap them.
 #include "device_utils.h"
 #include "gdn_internal.h"
 
@@ -35,12 +38,15 @@ namespace {
 
 template <int DK, int DV>
 struct DecodeShape {
-    static constexpr int NCW = (DV / 4) < 8 ? (DV / 4) : 8; // float4 columns per wave
-    static constexpr int LPC = 64 / NCW;                    // lanes splitting one column's keys
-    static constexpr int JPL = DK / LPC;                    // keys per lane
-    static constexpr int NW = DV / (4 * NCW);               // waves per head tile
+    static constexpr int LPR = DV / 4;                                 // lanes per key row (a float4 each)
+    static constexpr int RPI = 64 / LPR;                               // key rows per memory instruction
+    static constexpr int NWMAX = DK * DV / 1024;                       // waves with >= 4 rows per lane
+    static constexpr int NW = NWMAX < 1 ? 1 : (NWMAX > 4 ? 4 : NWMAX); // waves per workgroup
+    static constexpr int KPW = DK / NW;                                // key rows per wave
+    static constexpr int JPL = KPW / RPI;                              // key rows per lane
     static constexpr int NT = 64 * NW;
-    static_assert(JPL >= 1 && NW >= 1 && DK % LPC == 0, "unsupported head dims");
+    static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "value dim");
+    static_assert(DK % NW == 0 && KPW % RPI == 0 && JPL >= 1, "key dim");
 };
 
 struct DecodeParams {
@@ -78,16 +84,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(float* ssm, int byt
     return __builtin_amdgcn_make_buffer_rsrc(ssm, short(0), bytes, kBufferWord3);
 }
 
-// Tile of head h: key rows jl + LPC*m, value columns i0..i0+3 (voff = byte
-// offset of (jl, i0) inside a head tile).
-template <int DK, int DV, int JPL, int LPC>
+// Tile of head h: the lane's key rows RPI*m + (its first row), value columns
+// of its float4 (voff = byte offset of that first element inside a head tile).
+template <int DK, int DV, int JPL, int RPI>
 __device__ __forceinline__ void load_tile(f32x4 (&s)[JPL], __amdgpu_buffer_rsrc_t r, int voff,
                                           int h)
 {
 #pragma unroll
     for (int m = 0; m < JPL; ++m)
         s[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             r, voff, (h * DK + LPC * m) * DV * 4, kNonTemporal));
+                                             r, voff, (h * DK + RPI * m) * DV * 4, kNonTemporal));
 }
 
 // Stores take their whole offset in the VGPR and a literal zero soffset:
@@ -95,12 +101,22 @@ __device__ __forceinline__ void load_tile(f32x4 (&s)[JPL], __amdgpu_buffer_rsrc_
 // overwritten too early (the store reads them after issue) when soffset is
 // not an SGPR, and with an SGPR soffset that window was seen to corrupt the
 // last lanes' data.
-template <int DK, int DV, int LPC>
+template <int DK, int DV, int RPI>
 __device__ __forceinline__ void store_row(const f32x4& t, __amdgpu_buffer_rsrc_t r, int voff,
                                           int h, int m)
 {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t), r,
-                                           voff + (h * DK + LPC * m) * DV * 4, 0, kNonTemporal);
+                                           voff + (h * DK + RPI * m) * DV * 4, 0, kNonTemporal);
+}
+
+// Sum over the lanes l, l + S, l + 2S, ... of a wave (S a power of two).
+template <int S>
+__device__ __forceinline__ float strided_sum(float v)
+{
+#pragma unroll
+    for (int st = S; st < 64; st *= 2)
+        v += __shfl_xor(v, st, 64);
+    return v;
 }
 
 template <int JPL>
@@ -177,22 +193,25 @@ __device__ __forceinline__ void finish_conv_pair(const ConvPairIn<W>& in, uint32
 
 // One (row, k-head group).  WARM is a template parameter so that the cold
 // path (no state loads) and the warm path each get exact memory waits.
+// `red` holds the per-wave partial sums of S k and S q of two heads:
+// [2 heads][u | o][NW waves][DV].
 template <int DK, int DV, int W, bool WARM>
-__device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, int row, int g,
-                                             uint8_t* page)
+__device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, float* red, int row,
+                                             int g, uint8_t* page)
 {
     using Sh = DecodeShape<DK, DV>;
-    constexpr int JPL = Sh::JPL, LPC = Sh::LPC;
+    constexpr int JPL = Sh::JPL, RPI = Sh::RPI, LPR = Sh::LPR, NW = Sh::NW;
     const int G = p.Hv / p.Hk;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int jl = lane % LPC;
-    const int i0 = 4 * (wave * Sh::NCW + lane / LPC);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c4 = lane % LPR;                     // float4 column of the lane
+    const int key0 = wave * Sh::KPW + lane / LPR;  // first key row; then every RPI rows
     const int h0 = g * G;
     uint16_t* out_row = p.out + (int64_t(row) * p.Hv + h0) * DV;
     float* ssm = reinterpret_cast<float*>(page + p.ssm_off);
     const __amdgpu_buffer_rsrc_t rs = state_rsrc(ssm, p.Hv * DK * DV * 4);
-    const int voff = (jl * DV + i0) * 4;
+    const int voff = (key0 * DV + 4 * c4) * 4;
     uint16_t* win = reinterpret_cast<uint16_t*>(page + p.conv_off);
     const int C = p.C;
 
@@ -207,9 +226,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, i
     };
 
     // 1. conv inputs of the first channel pair, then the state tiles of the
-    //    first two heads: loads complete in issue order, so the conv runs
-    //    while the tiles are in flight, and the second tile arrives while
-    //    the first head is being processed
+    //    first two heads: the conv runs while the tiles are in flight
     ConvPairIn<W> cin;
     const int vc0 = 2 * tid;
     const int c0 = chan(vc0 < nvc ? vc0 : 0);
@@ -217,9 +234,9 @@ __device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, i
         load_conv_pair<W>(cin, p, row, c0, reinterpret_cast<const uint32_t*>(win + c0), WARM);
     f32x4 s0[JPL], s1[JPL];
     if constexpr (WARM) {
-        load_tile<DK, DV, JPL, LPC>(s0, rs, voff, h0);
+        load_tile<DK, DV, JPL, RPI>(s0, rs, voff, h0);
         if (G > 1)
-            load_tile<DK, DV, JPL, LPC>(s1, rs, voff, h0 + 1);
+            load_tile<DK, DV, JPL, RPI>(s1, rs, voff, h0 + 1);
     } else {
         zero_tile<JPL>(s0);
         zero_tile<JPL>(s1);
@@ -236,9 +253,9 @@ __device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, i
     }
     __syncthreads();
 
-    // 3. L2 norms and k.q; every wave reduces redundantly (no second barrier).
-    //    The dot products below run on the raw conv outputs; the norm factors
-    //    are applied to their sums.
+    // 3. L2 norms and k.q; every wave reduces redundantly.  The dot products
+    //    below run on the raw conv outputs; the norm factors are applied to
+    //    their sums.  The lane's raw k and q values stay in registers.
     float sq = 0.f, sk = 0.f, qk = 0.f;
     for (int j = lane; j < DK; j += 64) {
         const float a = ys[j], b = ys[DK + j];
@@ -252,57 +269,84 @@ __device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, i
     const float rq = p.scale / sqrtf(sq + p.eps);
     const float rk = 1.0f / sqrtf(sk + p.eps);
     const float kq = qk * rq * rk;
-    const float* qy = ys + jl;      // raw q of key jl + LPC*m at qy[LPC*m]
-    const float* ky = ys + DK + jl; // raw k likewise
+    float kr[JPL];
+#pragma unroll
+    for (int m = 0; m < JPL; ++m)
+        kr[m] = ys[DK + key0 + RPI * m];
 
-    // 4. gated delta rule for one v-head on the tile held in s
-    auto head = [&](f32x4 (&s)[JPL], int hh) {
-        const int h = h0 + hh;
+    // 4. the gated delta rule for a pair of v-heads (hh, hh+1) whose tiles
+    //    are held in s0, s1: partial sums, one exchange, then the update
+    auto partials = [&](const f32x4 (&s)[JPL], float* rh) {
         f32x4 u = f32x4{0.f, 0.f, 0.f, 0.f}, o = u;
 #pragma unroll
         for (int m = 0; m < JPL; ++m) {
-            u += s[m] * ky[LPC * m];
-            o += s[m] * qy[LPC * m];
+            u += s[m] * kr[m];
+            o += s[m] * ys[key0 + RPI * m];
         }
-        u.x = group_sum<LPC>(u.x);
-        u.y = group_sum<LPC>(u.y);
-        u.z = group_sum<LPC>(u.z);
-        u.w = group_sum<LPC>(u.w);
-        o.x = group_sum<LPC>(o.x);
-        o.y = group_sum<LPC>(o.y);
-        o.z = group_sum<LPC>(o.z);
-        o.w = group_sum<LPC>(o.w);
+        u.x = strided_sum<LPR>(u.x);
+        u.y = strided_sum<LPR>(u.y);
+        u.z = strided_sum<LPR>(u.z);
+        u.w = strided_sum<LPR>(u.w);
+        o.x = strided_sum<LPR>(o.x);
+        o.y = strided_sum<LPR>(o.y);
+        o.z = strided_sum<LPR>(o.z);
+        o.w = strided_sum<LPR>(o.w);
+        if (lane < LPR) {
+            *reinterpret_cast<f32x4*>(rh + wave * DV + 4 * c4) = u;
+            *reinterpret_cast<f32x4*>(rh + (NW + wave) * DV + 4 * c4) = o;
+        }
+    };
+    auto finish = [&](const f32x4 (&s)[JPL], const float* rh, int hh) {
+        const int h = h0 + hh;
+        f32x4 u = f32x4{0.f, 0.f, 0.f, 0.f}, o = u;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            u += *reinterpret_cast<const f32x4*>(rh + w * DV + 4 * c4);
+            o += *reinterpret_cast<const f32x4*>(rh + (NW + w) * DV + 4 * c4);
+        }
         const float a = p.alpha[int64_t(row) * p.Hv + h];
         const float b = p.beta[int64_t(row) * p.Hv + h];
-        const f32x4 v = *reinterpret_cast<const f32x4*>(ys + 2 * DK + hh * DV + i0);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ys + 2 * DK + hh * DV + 4 * c4);
         // d = b (v - a S k^), with k^ = rk k
         const f32x4 d = b * (v - (a * rk) * u);
         const f32x4 dk = d * rk; // update S <- a S + d k^T with raw k
 #pragma unroll
-        for (int m = 0; m < JPL; ++m) {
-            store_row<DK, DV, LPC>(a * s[m] + dk * ky[LPC * m], rs, voff, h, m);
-        }
-        if (jl == 0) {
+        for (int m = 0; m < JPL; ++m)
+            store_row<DK, DV, RPI>(a * s[m] + dk * kr[m], rs, voff, h, m);
+        if (wave == 0 && lane < LPR) {
             // o = a S q^ + d (k^.q^), with q^ = rq q
             const f32x4 ov = (a * rq) * o + d * kq;
-            *reinterpret_cast<uint2*>(out_row + hh * DV + i0) = pack_bf16x4(ov.x, ov.y, ov.z, ov.w);
+            *reinterpret_cast<uint2*>(out_row + hh * DV + 4 * c4) =
+                pack_bf16x4(ov.x, ov.y, ov.z, ov.w);
         }
     };
-    head(s0, 0);
-    if (G > 1)
-        head(s1, 1);
-    for (int hh = 2; hh < G; ++hh) { // groups wider than two heads: one tile at a time
-        if constexpr (WARM)
-            load_tile<DK, DV, JPL, LPC>(s0, rs, voff, h0 + hh);
-        head(s0, hh);
+    constexpr int RH = 2 * NW * DV; // floats of one head's partial sums
+    for (int hh = 0; hh < G; hh += 2) {
+        const bool pair = hh + 1 < G;
+        if (hh > 0) { // the next pair's tiles; red is free again after the barrier
+            if constexpr (WARM) {
+                load_tile<DK, DV, JPL, RPI>(s0, rs, voff, h0 + hh);
+                if (pair)
+                    load_tile<DK, DV, JPL, RPI>(s1, rs, voff, h0 + hh + 1);
+            }
+            __syncthreads();
+        }
+        partials(s0, red);
+        if (pair)
+            partials(s1, red + RH);
+        __syncthreads();
+        finish(s0, red, hh);
+        if (pair)
+            finish(s1, red + RH, hh + 1);
     }
 }
 
 template <int DK, int DV, int W>
-__global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(DecodeParams p)
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_kernel(DecodeParams p)
 {
     using Sh = DecodeShape<DK, DV>;
-    extern __shared__ float ys[]; // conv outputs: q (DK) | k (DK) | v (G*DV)
+    extern __shared__ float ys[]; // conv outputs: q (DK) | k (DK) | v (G*DV); partial sums
     const int row = blockIdx.x / p.Hk;
     const int g = blockIdx.x - row * p.Hk;
     const int slot = p.state_indices[row];
@@ -314,10 +358,11 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(Decod
         return;
     }
     uint8_t* page = p.layer + int64_t(slot) * p.page_stride;
+    float* red = ys + 2 * DK + (p.Hv / p.Hk) * DV;
     if (p.hs[row] != 0)
-        decode_group<DK, DV, W, true>(p, ys, row, g, page);
+        decode_group<DK, DV, W, true>(p, ys, red, row, g, page);
     else
-        decode_group<DK, DV, W, false>(p, ys, row, g, page);
+        decode_group<DK, DV, W, false>(p, ys, red, row, g, page);
 }
 
 template <int DK, int DV, int W>
@@ -346,7 +391,7 @@ int launch_decode_t(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn
     p.scale = a->scale;
     p.eps = a->l2_eps;
     const int G = d.num_v_heads / d.num_k_heads;
-    const size_t lds = sizeof(float) * size_t(2 * DK + G * DV);
+    const size_t lds = sizeof(float) * size_t(2 * DK + G * DV + 2 * 2 * Sh::NW * DV);
     const int64_t blocks = int64_t(rows) * d.num_k_heads;
     if (blocks > INT32_MAX)
         return fail(GDN_ERANGE, "decode grid too large");

@@ -166,6 +166,37 @@ def bench_restore(steps, warmup):
     return ms, nbytes, hits, int(linear.sum())
 
 
+def bench_slot_manager(rows=256, steps=200):
+    """Host cost of one scheduler step of the slot manager: resolve + commit of
+    a 256-row batch in which every row asks for a restore and a save.  The
+    request arrays are built beforehand; the timed loop makes only the two
+    C-ABI calls per step."""
+    import ctypes
+
+    import hybrid_linear_attention_slot_amd as gdn
+    L = gdn.lib()
+    m = gdn.gdn_slots_create(4 * rows, 16)
+    for q in range(rows):
+        gdn.gdn_slots_add_sequence(m, q)
+    reqs = []
+    for st in range(steps):
+        arr = (gdn.gdn_slot_request * rows)(
+            *[gdn.gdn_slot_request(q, 16 * st, 16 * st + 16, (st << 20) + q + 1,
+                                   ((st + 1) << 20) + q + 1) for q in range(rows)])
+        reqs.append(arr)
+    ops = (gdn.gdn_linear_state_op * rows)()
+    t0 = time.perf_counter()
+    for arr in reqs:
+        if L.gdn_slots_resolve(m.handle, arr, rows, ops) != 0 or L.gdn_slots_commit(m.handle) != 0:
+            raise RuntimeError(gdn.gdn_last_error())
+    dt = time.perf_counter() - t0
+    gdn.gdn_slots_destroy(m)
+    return {"us_per_step": round(dt / steps * 1e6, 2), "rows": rows,
+            "note": "resolve + commit (C-ABI calls only) of 256 rows that all request a "
+                    "save and a restore; 1024 slots, so the first steps promote every row "
+                    "and later ones match restores and skip saves for want of free slots"}
+
+
 def cpu_baseline(inp_decode, min_seconds=10.0):
     """The oracle on this host, on the decode batch, repeated for >= min_seconds."""
     import dataclasses
@@ -263,6 +294,7 @@ def main():
         "prefill": prefill,
         "restore": restore,
     }
+    line["slot_manager"] = bench_slot_manager()
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)

@@ -23,10 +23,14 @@ GDN_EOVERLAP = -3
 GDN_EALIGN = -4
 GDN_EUNSUPPORTED = -5
 GDN_EHIP = -6
+GDN_ENOSLOT = -7
+GDN_ESTATE = -8
 
 ERROR_NAMES = {GDN_EINVAL: "GDN_EINVAL", GDN_ERANGE: "GDN_ERANGE", GDN_EOVERLAP: "GDN_EOVERLAP",
                GDN_EALIGN: "GDN_EALIGN", GDN_EUNSUPPORTED: "GDN_EUNSUPPORTED",
-               GDN_EHIP: "GDN_EHIP"}
+               GDN_EHIP: "GDN_EHIP", GDN_ENOSLOT: "GDN_ENOSLOT", GDN_ESTATE: "GDN_ESTATE"}
+
+GDN_SLOT_FREE, GDN_SLOT_LIVE, GDN_SLOT_CHECKPOINT, GDN_SLOT_RESERVED = 0, 1, 2, 3
 
 
 class GdnError(RuntimeError):
@@ -61,6 +65,21 @@ class gdn_step_args(C.Structure):
                 ("scale", C.c_float), ("l2_eps", C.c_float)]
 
 
+class gdn_slot_request(C.Structure):
+    _fields_ = [("seq_id", C.c_int64), ("n_kv_cache_tokens", C.c_int64),
+                ("n_tokens_after_step", C.c_int64), ("restore_prefix_hash", C.c_uint64),
+                ("save_prefix_hash", C.c_uint64)]
+
+
+class gdn_linear_state_op(C.Structure):
+    _fields_ = [("linear_state_id", C.c_int32), ("restore_src_slot_id", C.c_int32),
+                ("save_dst_slot_id", C.c_int32), ("has_initial_state", C.c_int32),
+                ("restore_prefix_hash", C.c_uint64), ("save_prefix_hash", C.c_uint64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
 _lib = None
 
 
@@ -93,6 +112,29 @@ def lib() -> C.CDLL:
         L.gdn_prefill_varlen.restype = C.c_int
         L.gdn_last_error.argtypes = []
         L.gdn_last_error.restype = C.c_char_p
+        u64 = C.c_uint64
+        L.gdn_slots_create.argtypes = [i32, i32, C.POINTER(C.c_void_p)]
+        L.gdn_slots_destroy.argtypes = [p]
+        L.gdn_slots_destroy.restype = None
+        L.gdn_slots_add_sequence.argtypes = [p, i64, C.POINTER(i32)]
+        L.gdn_slots_remove_sequence.argtypes = [p, i64]
+        L.gdn_slots_resolve.argtypes = [p, C.POINTER(gdn_slot_request), i32,
+                                        C.POINTER(gdn_linear_state_op)]
+        L.gdn_slots_commit.argtypes = [p]
+        L.gdn_slots_abort.argtypes = [p]
+        L.gdn_slots_restore_ops.argtypes = [C.POINTER(gdn_linear_state_op), i32,
+                                            C.POINTER(gdn_restore_op)]
+        L.gdn_slots_slot_info.argtypes = [p, i32, C.POINTER(i32), C.POINTER(i64), C.POINTER(u64),
+                                          C.POINTER(i32)]
+        L.gdn_slots_sequence_info.argtypes = [p, i64, C.POINTER(i32), C.POINTER(i32)]
+        L.gdn_slots_lookup.argtypes = [p, u64]
+        L.gdn_slots_lookup.restype = i32
+        L.gdn_slots_counts.argtypes = [p, C.POINTER(i32)]
+        for f in ("gdn_slots_create", "gdn_slots_add_sequence", "gdn_slots_remove_sequence",
+                  "gdn_slots_resolve", "gdn_slots_commit", "gdn_slots_abort",
+                  "gdn_slots_restore_ops", "gdn_slots_slot_info", "gdn_slots_sequence_info",
+                  "gdn_slots_counts"):
+            getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
 
@@ -221,3 +263,96 @@ def gdn_prefill_varlen(pool: Pool, layer: int, num_seqs: int, cu_seqlens, max_se
     return _check(lib().gdn_prefill_varlen(pool.handle, layer, num_seqs, _addr(cu_seqlens),
                                            max_seqlen, total_tokens, C.byref(args),
                                            _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Host-side slot manager of the prefix cache (include/gdn_slots.h)
+# ---------------------------------------------------------------------------
+class SlotManager:
+    """Owner of a gdn_slot_manager handle."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+
+    def close(self):
+        if self.handle:
+            lib().gdn_slots_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gdn_slots_create(num_slots: int, block_size: int) -> SlotManager:
+    h = C.c_void_p()
+    _check(lib().gdn_slots_create(num_slots, block_size, C.byref(h)))
+    return SlotManager(h.value)
+
+
+def gdn_slots_destroy(m: SlotManager) -> None:
+    m.close()
+
+
+def gdn_slots_add_sequence(m: SlotManager, seq_id: int) -> int:
+    s = C.c_int32()
+    _check(lib().gdn_slots_add_sequence(m.handle, seq_id, C.byref(s)))
+    return s.value
+
+
+def gdn_slots_remove_sequence(m: SlotManager, seq_id: int) -> None:
+    _check(lib().gdn_slots_remove_sequence(m.handle, seq_id))
+
+
+def gdn_slots_resolve(m: SlotManager, rows) -> list:
+    """rows: sequence of (seq_id, n_kv_cache_tokens, n_tokens_after_step,
+    restore_prefix_hash, save_prefix_hash).  Returns the ops as dicts."""
+    rows = [tuple(int(v) for v in r) for r in rows]
+    n = len(rows)
+    arr = (gdn_slot_request * max(1, n))(*[gdn_slot_request(*r) for r in rows])
+    ops = (gdn_linear_state_op * max(1, n))()
+    _check(lib().gdn_slots_resolve(m.handle, arr, n, ops))
+    return [ops[i].as_dict() for i in range(n)]
+
+
+def gdn_slots_commit(m: SlotManager) -> None:
+    _check(lib().gdn_slots_commit(m.handle))
+
+
+def gdn_slots_abort(m: SlotManager) -> None:
+    _check(lib().gdn_slots_abort(m.handle))
+
+
+def gdn_slots_restore_ops(ops) -> list:
+    """ops: the dicts gdn_slots_resolve returned; returns (dst, src, requested) tuples."""
+    n = len(ops)
+    arr = (gdn_linear_state_op * max(1, n))(
+        *[gdn_linear_state_op(**{f: o[f] for f, _ in gdn_linear_state_op._fields_}) for o in ops])
+    out = (gdn_restore_op * max(1, n))()
+    _check(lib().gdn_slots_restore_ops(arr, n, out))
+    return [(out[i].dst_slot, out[i].src_slot, out[i].requested) for i in range(n)]
+
+
+def gdn_slots_slot_info(m: SlotManager, slot: int):
+    k, o, h, p = C.c_int32(), C.c_int64(), C.c_uint64(), C.c_int32()
+    _check(lib().gdn_slots_slot_info(m.handle, slot, C.byref(k), C.byref(o), C.byref(h),
+                                     C.byref(p)))
+    return k.value, o.value, h.value, p.value
+
+
+def gdn_slots_sequence_info(m: SlotManager, seq_id: int):
+    s, i = C.c_int32(), C.c_int32()
+    _check(lib().gdn_slots_sequence_info(m.handle, seq_id, C.byref(s), C.byref(i)))
+    return s.value, i.value
+
+
+def gdn_slots_lookup(m: SlotManager, prefix_hash: int) -> int:
+    return int(lib().gdn_slots_lookup(m.handle, prefix_hash))
+
+
+def gdn_slots_counts(m: SlotManager) -> list:
+    c = (C.c_int32 * 4)()
+    _check(lib().gdn_slots_counts(m.handle, c))
+    return list(c)

@@ -141,7 +141,18 @@ def bench_prefill(steps, warmup):
     ms = timed(lambda: gdn.gdn_prefill_varlen(h, 0, inp.num_seqs, cu, inp.max_seqlen,
                                               inp.total_tokens, args, stream),
                max(2, steps // 5), max(1, warmup // 5), stream)
-    return inp, ms
+    # the same call emitting every sequence's state at its last 256-token block
+    # boundary into a spare slot
+    lens = np.diff(inp.cu_seqlens)
+    used = set(inp.state_indices.tolist())
+    ck_slot = dev(np.array([s for s in range(g.num_slots) if s not in used][:inp.num_seqs],
+                           np.int32))
+    ck_len = dev((lens // 256 * 256).astype(np.int32))
+    ms_ck = timed(lambda: gdn.gdn_prefill_varlen_checkpoint(h, 0, inp.num_seqs, cu,
+                                                            inp.max_seqlen, inp.total_tokens,
+                                                            args, ck_slot, ck_len, stream),
+                  max(2, steps // 5), max(1, warmup // 5), stream)
+    return inp, ms, ms_ck
 
 
 def bench_restore(steps, warmup):
@@ -256,14 +267,17 @@ def main():
         torch.cuda.empty_cache()
     inp, ms, nbytes = bench_decode(a.steps, a.warmup)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    pinp, pms = bench_prefill(a.steps, a.warmup)
+    pinp, pms, pms_ck = bench_prefill(a.steps, a.warmup)
     prefill = {"tokens_per_s": round(pinp.total_tokens / (pms * 1e-3), 1),
                "ms_per_call": round(pms, 4), "tokens": pinp.total_tokens,
                "max_seqlen": pinp.max_seqlen,
                "us_per_token_critical_path": round(pms * 1e3 / pinp.max_seqlen, 4),
                "gb_per_s": round(prefill_bytes(pinp) / (pms * 1e-3) / 1e9, 2),
                "workload": "8 seqs, lengths U{512..4096}, 16 v-heads/8 k-heads, 128x128 fp32, "
-                           "4 warm + 4 cold"}
+                           "4 warm + 4 cold",
+               "ms_per_call_with_checkpoints": round(pms_ck, 4),
+               "checkpoints": "each sequence's state at its last 256-token boundary emitted "
+                              "into a spare slot (gdn_prefill_varlen_checkpoint)"}
     restore = None
     if not a.no_restore:
         rms, rbytes, hits, nlin = bench_restore(a.steps, a.warmup)

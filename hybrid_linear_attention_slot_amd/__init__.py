@@ -110,6 +110,9 @@ def lib() -> C.CDLL:
         L.gdn_decode_step.restype = C.c_int
         L.gdn_prefill_varlen.argtypes = [p, i32, i32, p, i32, i64, C.POINTER(gdn_step_args), p]
         L.gdn_prefill_varlen.restype = C.c_int
+        L.gdn_prefill_varlen_checkpoint.argtypes = [p, i32, i32, p, i32, i64,
+                                                    C.POINTER(gdn_step_args), p, p, p]
+        L.gdn_prefill_varlen_checkpoint.restype = C.c_int
         L.gdn_last_error.argtypes = []
         L.gdn_last_error.restype = C.c_char_p
         u64 = C.c_uint64
@@ -263,6 +266,14 @@ def gdn_prefill_varlen(pool: Pool, layer: int, num_seqs: int, cu_seqlens, max_se
     return _check(lib().gdn_prefill_varlen(pool.handle, layer, num_seqs, _addr(cu_seqlens),
                                            max_seqlen, total_tokens, C.byref(args),
                                            _stream(stream)))
+
+
+def gdn_prefill_varlen_checkpoint(pool: Pool, layer: int, num_seqs: int, cu_seqlens,
+                                  max_seqlen: int, total_tokens: int, args: gdn_step_args,
+                                  ckpt_slot, ckpt_len, stream=None) -> int:
+    return _check(lib().gdn_prefill_varlen_checkpoint(
+        pool.handle, layer, num_seqs, _addr(cu_seqlens), max_seqlen, total_tokens,
+        C.byref(args), _addr(ckpt_slot), _addr(ckpt_len), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -318,11 +318,12 @@ int gdn_decode_step(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn
     return gdn::launch_decode(pool, layer, rows, a, reinterpret_cast<hipStream_t>(stream));
 }
 
-int gdn_prefill_varlen(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
-                       const int32_t* cu_seqlens, int32_t max_seqlen, int64_t total_tokens,
-                       const gdn_step_args* a, gdn_stream_t stream)
+namespace {
+int prefill_common(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
+                   const int32_t* cu_seqlens, int32_t max_seqlen, int64_t total_tokens,
+                   const gdn_step_args* a, const int32_t* ckpt_slot, const int32_t* ckpt_len,
+                   gdn_stream_t stream)
 {
-    gdn::clear_error();
     if (!pool)
         return fail(GDN_EINVAL, "pool is NULL");
     if (num_seqs < 0 || max_seqlen < 0 || total_tokens < 0)
@@ -343,8 +344,31 @@ int gdn_prefill_varlen(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
     if ((reinterpret_cast<uintptr_t>(a->conv_w) & 3u) != 0 ||
         (reinterpret_cast<uintptr_t>(a->conv_b) & 3u) != 0)
         return fail(GDN_EALIGN, "conv_w and conv_b must be 4-byte aligned");
-    return gdn::launch_prefill(pool, layer, num_seqs, cu_seqlens, a,
+    return gdn::launch_prefill(pool, layer, num_seqs, cu_seqlens, a, ckpt_slot, ckpt_len,
                                reinterpret_cast<hipStream_t>(stream));
+}
+} // namespace
+
+int gdn_prefill_varlen(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
+                       const int32_t* cu_seqlens, int32_t max_seqlen, int64_t total_tokens,
+                       const gdn_step_args* a, gdn_stream_t stream)
+{
+    gdn::clear_error();
+    return prefill_common(pool, layer, num_seqs, cu_seqlens, max_seqlen, total_tokens, a,
+                          nullptr, nullptr, stream);
+}
+
+int gdn_prefill_varlen_checkpoint(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
+                                  const int32_t* cu_seqlens, int32_t max_seqlen,
+                                  int64_t total_tokens, const gdn_step_args* a,
+                                  const int32_t* ckpt_slot_dev, const int32_t* ckpt_len_dev,
+                                  gdn_stream_t stream)
+{
+    gdn::clear_error();
+    if (!ckpt_slot_dev || !ckpt_len_dev)
+        return fail(GDN_EINVAL, "ckpt_slot and ckpt_len must not be NULL");
+    return prefill_common(pool, layer, num_seqs, cu_seqlens, max_seqlen, total_tokens, a,
+                          ckpt_slot_dev, ckpt_len_dev, stream);
 }
 
 } // extern "C"

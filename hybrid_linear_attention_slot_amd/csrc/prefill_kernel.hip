@@ -89,6 +89,8 @@ struct PrefillParams {
     const int32_t* state_indices;
     const uint8_t* hs;
     uint16_t* out;
+    const int32_t* ckpt_slot; // NULL, or per sequence: page that receives the
+    const int32_t* ckpt_len;  // state after the first ckpt_len tokens
     float scale;
     float eps;
 };
@@ -103,7 +105,9 @@ __device__ __forceinline__ int ring_pos(int t) // t >= -RING
 }
 
 template <int DK, int DV, int W>
-__global__ __launch_bounds__((PrefillShape<DK, DV>::NT)) void prefill_kernel(PrefillParams p)
+// four waves per SIMD: two 512-thread workgroups per CU (their LDS fits too)
+__global__ __launch_bounds__((PrefillShape<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4)))
+void prefill_kernel(PrefillParams p)
 {
     using Sh = PrefillShape<DK, DV>;
     constexpr int KPL = Sh::KPL, LPC = Sh::LPC, CPW = Sh::CPW, NCONS = Sh::NCONS;
@@ -219,13 +223,39 @@ __global__ __launch_bounds__((PrefillShape<DK, DV>::NT)) void prefill_kernel(Pre
             if (jl == 0)
                 ob[buf][tt][col] = ov;
         };
+        // checkpoint emission: the state after token ck_tok (if any) is also
+        // stored into the checkpoint page
+        // (buffer stores: one VGPR offset per lane and per-store constants, so
+        // the rarely used path holds no addresses across the token loop)
+        int ck_tok = -1;
+        float* ck_tile = tile;
+        if (p.ckpt_slot) {
+            const int cs = p.ckpt_slot[n], cl = p.ckpt_len[n];
+            if (cs >= 0 && cs < p.num_slots && cl >= 1 && cl <= L) {
+                ck_tok = cl - 1;
+                ck_tile = reinterpret_cast<float*>(p.layer + int64_t(cs) * p.page_stride + p.ssm_off) +
+                          int64_t(h) * DK * DV;
+            }
+        }
+        const __amdgpu_buffer_rsrc_t ck_rs = __builtin_amdgcn_make_buffer_rsrc(
+            ck_tile, short(0), ck_tok >= 0 ? DK * DV * 4 : 0, 0x00020000);
+        const int voff = (4 * jl * DV + gcol) * 4;
+        auto store_ck = [&]() {
+#pragma unroll
+            for (int m = 0; m < KPL / 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __float_as_uint(s[4 * m + e]), ck_rs,
+                        voff + (4 * LPC * m + e) * DV * 4, 0, 0);
+        };
         __syncthreads(); // A: history and chunk 0 staged
         __syncthreads(); // B: chunk 0 prepared
         for (int c = 0; c < nchunks; ++c) {
             const int buf = c & 1;
             const int nt = chunk_len(c);
             Ops A, B;
-            if (nt == CT) {
+            if (nt == CT && ck_tok / CT != c) {
                 // full chunk: a fixed-trip loop without branches, so that each
                 // token waits only for its own operands (the last fetch of the
                 // chunk re-reads token CT-1 and is unused)
@@ -236,10 +266,12 @@ __global__ __launch_bounds__((PrefillShape<DK, DV>::NT)) void prefill_kernel(Pre
                     fetch(A, buf, min(tt + 2, CT - 1));
                     step(B, buf, tt + 1);
                 }
-            } else {
+            } else { // a ragged last chunk, or the chunk holding the checkpoint token
                 for (int tt = 0; tt < nt; ++tt) {
                     fetch(A, buf, tt);
                     step(A, buf, tt);
+                    if (c * CT + tt == ck_tok)
+                        store_ck();
                 }
             }
             __syncthreads();
@@ -484,6 +516,8 @@ struct WindowParams {
     const uint16_t* x;
     const int32_t* state_indices;
     const uint8_t* hs;
+    const int32_t* ckpt_slot; // as in PrefillParams
+    const int32_t* ckpt_len;
 };
 
 constexpr int kWinThreads = 256;
@@ -503,24 +537,41 @@ __global__ __launch_bounds__(kWinThreads) void prefill_window_kernel(WindowParam
     const bool warm = p.hs[n] != 0;
     uint16_t* win = reinterpret_cast<uint16_t*>(p.layer + int64_t(slot) * p.page_stride +
                                                 p.conv_off);
-    uint16_t nw[7];
+    // the window after the first `len` tokens: the last W-1 of (old window, x)
+    auto window_at = [&](int len, uint16_t (&nw)[7]) {
 #pragma unroll
-    for (int w = 0; w < 7; ++w) {
-        if (w < p.W - 1) {
-            const int pos = L - (p.W - 1) + w; // position relative to the first token
-            nw[w] = pos >= 0 ? p.x[int64_t(tb + pos) * p.C + c]
-                             : (warm ? win[int64_t(p.W - 1 + pos) * p.C + c] : uint16_t(0));
+        for (int w = 0; w < 7; ++w) {
+            if (w < p.W - 1) {
+                const int pos = len - (p.W - 1) + w; // position relative to the first token
+                nw[w] = pos >= 0 ? p.x[int64_t(tb + pos) * p.C + c]
+                                 : (warm ? win[int64_t(p.W - 1 + pos) * p.C + c] : uint16_t(0));
+            }
+        }
+    };
+    uint16_t nw[7], cw[7];
+    window_at(L, nw);
+    uint16_t* ck_win = nullptr;
+    if (p.ckpt_slot) {
+        const int cs = p.ckpt_slot[n], cl = p.ckpt_len[n];
+        if (cs >= 0 && cs < p.num_slots && cl >= 1 && cl <= L) {
+            window_at(cl, cw); // reads the old window before it is rewritten below
+            ck_win = reinterpret_cast<uint16_t*>(p.layer + int64_t(cs) * p.page_stride + p.conv_off);
         }
     }
 #pragma unroll
-    for (int w = 0; w < 7; ++w)
-        if (w < p.W - 1)
+    for (int w = 0; w < 7; ++w) {
+        if (w < p.W - 1) {
             win[int64_t(w) * p.C + c] = nw[w];
+            if (ck_win)
+                ck_win[int64_t(w) * p.C + c] = cw[w];
+        }
+    }
 }
 
 template <int DK, int DV, int W>
 int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, const int32_t* cu,
-                     const gdn_step_args* a, hipStream_t stream)
+                     const gdn_step_args* a, const int32_t* ckpt_slot, const int32_t* ckpt_len,
+                     hipStream_t stream)
 {
     using Sh = PrefillShape<DK, DV>;
     const gdn_pool_desc& d = pool->desc;
@@ -543,6 +594,8 @@ int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, cons
     p.state_indices = a->state_indices;
     p.hs = a->has_initial_state;
     p.out = a->out;
+    p.ckpt_slot = ckpt_slot;
+    p.ckpt_len = ckpt_len;
     p.scale = a->scale;
     p.eps = a->l2_eps;
     const int64_t blocks = int64_t(num_seqs) * d.num_v_heads * Sh::NSL;
@@ -564,6 +617,8 @@ int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, cons
     w.x = a->x;
     w.state_indices = a->state_indices;
     w.hs = a->has_initial_state;
+    w.ckpt_slot = ckpt_slot;
+    w.ckpt_len = ckpt_len;
     const int64_t wblocks =
         int64_t(num_seqs) * ((d.conv_channels + kWinThreads - 1) / kWinThreads);
     if (wblocks > INT32_MAX)
@@ -575,12 +630,12 @@ int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, cons
 
 template <int DK>
 int dispatch_w(const gdn_pool* pool, int32_t layer, int32_t num_seqs, const int32_t* cu,
-               const gdn_step_args* a, hipStream_t stream)
+               const gdn_step_args* a, const int32_t* cs, const int32_t* cl, hipStream_t stream)
 {
     switch (pool->desc.conv_width) {
-    case 2: return launch_prefill_t<DK, DK, 2>(pool, layer, num_seqs, cu, a, stream);
-    case 3: return launch_prefill_t<DK, DK, 3>(pool, layer, num_seqs, cu, a, stream);
-    case 4: return launch_prefill_t<DK, DK, 4>(pool, layer, num_seqs, cu, a, stream);
+    case 2: return launch_prefill_t<DK, DK, 2>(pool, layer, num_seqs, cu, a, cs, cl, stream);
+    case 3: return launch_prefill_t<DK, DK, 3>(pool, layer, num_seqs, cu, a, cs, cl, stream);
+    case 4: return launch_prefill_t<DK, DK, 4>(pool, layer, num_seqs, cu, a, cs, cl, stream);
     default: return fail(GDN_EUNSUPPORTED, "prefill: conv width %d", pool->desc.conv_width);
     }
 }
@@ -593,13 +648,15 @@ bool prefill_supported(int dk, int dv, int W)
 }
 
 int launch_prefill(const gdn_pool* pool, int32_t layer, int32_t num_seqs, const int32_t* cu,
-                   const gdn_step_args* a, hipStream_t stream)
+                   const gdn_step_args* a, const int32_t* ckpt_slot, const int32_t* ckpt_len,
+                   hipStream_t stream)
 {
+    const int32_t *cs = ckpt_slot, *cl = ckpt_len;
     switch (pool->desc.head_k_dim) {
-    case 16: return dispatch_w<16>(pool, layer, num_seqs, cu, a, stream);
-    case 32: return dispatch_w<32>(pool, layer, num_seqs, cu, a, stream);
-    case 64: return dispatch_w<64>(pool, layer, num_seqs, cu, a, stream);
-    case 128: return dispatch_w<128>(pool, layer, num_seqs, cu, a, stream);
+    case 16: return dispatch_w<16>(pool, layer, num_seqs, cu, a, cs, cl, stream);
+    case 32: return dispatch_w<32>(pool, layer, num_seqs, cu, a, cs, cl, stream);
+    case 64: return dispatch_w<64>(pool, layer, num_seqs, cu, a, cs, cl, stream);
+    case 128: return dispatch_w<128>(pool, layer, num_seqs, cu, a, cs, cl, stream);
     default: return fail(GDN_EUNSUPPORTED, "prefill: head dim %d", pool->desc.head_k_dim);
     }
 }

@@ -196,6 +196,25 @@ int gdn_prefill_varlen(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
                        const int32_t* cu_seqlens_dev, int32_t max_seqlen, int64_t total_tokens,
                        const gdn_step_args* args, gdn_stream_t stream);
 
+/* Varlen prefill that also writes a block-boundary checkpoint ("Linear-State
+ * Prefix Cache 内部机制" §3.1: the checkpoint is the recurrent state at a
+ * block-aligned boundary; here the boundary may fall inside the chunk the
+ * call computes, so the state there is emitted into a separate page instead
+ * of being lost).  Sequence n with 0 <= ckpt_slot_dev[n] < num_slots and
+ * 1 <= ckpt_len_dev[n] <= its length gets, in page ckpt_slot_dev[n], the
+ * window and state after its first ckpt_len_dev[n] tokens (payload only;
+ * padding untouched); other values mean no checkpoint for that sequence.
+ * ckpt_slot_dev, ckpt_len_dev: device int32 [num_seqs], both non-NULL
+ * (GDN_EINVAL).  A checkpoint slot must differ from every state_indices
+ * entry and from the other checkpoint slots of the call (not checkable on
+ * the host; two writers of one page race).  Everything else as
+ * gdn_prefill_varlen, whose results it leaves unchanged. */
+int gdn_prefill_varlen_checkpoint(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
+                                  const int32_t* cu_seqlens_dev, int32_t max_seqlen,
+                                  int64_t total_tokens, const gdn_step_args* args,
+                                  const int32_t* ckpt_slot_dev, const int32_t* ckpt_len_dev,
+                                  gdn_stream_t stream);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char* gdn_last_error(void);
 

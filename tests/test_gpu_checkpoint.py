@@ -1,0 +1,131 @@
+"""Block-boundary checkpoint emission inside a varlen prefill
+(gdn_prefill_varlen_checkpoint), through the C-ABI.
+
+For each sequence with a checkpoint request the page ckpt_slot must hold,
+after the call, the window and state the sequence had after its first
+ckpt_len tokens -- that is, what a prefill of just those tokens leaves in the
+sequence's own page.  Checked against the oracle's prefix runs (small shapes,
+every head size, ragged lengths, requests at token 1, at chunk edges, at the
+end, and ignored ones) and, at the 8-sequence workload's full size, bit for
+bit against a separate GPU prefill of the prefixes.  The call's ordinary
+results must be those of gdn_prefill_varlen.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_linear_attention_slot_amd as gdn
+import oracle
+import workloads as wl
+from gpu_util import (DevicePool, check_outputs, check_pages, log, step_tensors, to_dev, u16,
+                      args_of)
+
+pytestmark = pytest.mark.gpu
+
+DIMS = [(1, 2, 16), (2, 4, 32), (2, 2, 64), (4, 8, 128)]
+
+
+def oracle_prefix_page(img, inp, n, length):
+    """Page of sequence n after its first `length` tokens (oracle)."""
+    g = inp.geom
+    t0 = int(inp.cu_seqlens[n])
+    sub = dataclasses.replace(g, num_slots=1)
+    page = img[int(inp.state_indices[n])][None].copy()
+    sl = slice(t0, t0 + length)
+    oracle.gdn_layer(page, sub, np.array([0, length], np.int32), np.zeros(1, np.int32),
+                     inp.has_initial_state[n:n + 1], inp.x[sl], inp.conv_w, inp.conv_b,
+                     inp.alpha[sl], inp.beta[sl], inp.scale, inp.eps)
+    return page
+
+
+@pytest.mark.parametrize("Hk,Hv,d", DIMS)
+def test_checkpoint_emission_matches_oracle_prefix(Hk, Hv, d):
+    g = wl.make_geometry(16, Hk=Hk, Hv=Hv, dk=d, dv=d, W=4, page_align=128, extra_pad=128)
+    rng = wl.rng_for(300 + d)
+    lens = [70, 1, 33, 40, 0, 97, 32]
+    warm = [1, 0, 1, 1, 0, 0, 1]
+    perm = rng.permutation(g.num_slots).astype(np.int32)
+    idx, spare = perm[:7], perm[7:]
+    # requests: mid-chunk, first token, at the end, at a chunk edge, on an empty
+    # sequence (ignored), past the end (ignored), none
+    ck_len = np.array([23, 1, 33, 16, 1, 98, 0], np.int32)
+    ck_slot = np.array([spare[0], spare[1], spare[2], spare[3], spare[4], spare[5], -1], np.int32)
+    valid = [0, 1, 2, 3]
+    hs = np.asarray(warm, np.uint8)
+    img = wl.make_pool_image(g, rng, warm_slots=idx[hs == 1], nan_slots=idx[hs == 0], sigma_s=0.5)
+    inp = wl.step_inputs(g, rng, lens, idx, hs, bias=True)
+    inp.scale = 0.8
+    dp = DevicePool(g, [img])
+    t = step_tensors(inp)
+    log(f"checkpoint emission d={d}")
+    rc = gdn.gdn_prefill_varlen_checkpoint(dp.pool, 0, inp.num_seqs, t["cu"], inp.max_seqlen,
+                                           inp.total_tokens, args_of(t, inp), to_dev(ck_slot),
+                                           to_dev(ck_len))
+    assert rc == gdn.GDN_OK
+    torch.cuda.synchronize()
+    got = dp.host()
+    # the ordinary results, and every page that is neither a sequence's nor a
+    # valid checkpoint's, as the oracle says
+    ref = img.copy()
+    o64, _ = oracle.gdn_layer(ref, g, inp.cu_seqlens, inp.state_indices, inp.has_initial_state,
+                              inp.x, inp.conv_w, inp.conv_b, inp.alpha, inp.beta, inp.scale,
+                              inp.eps)
+    check_outputs(u16(t["out"]), o64, f"d={d} outputs")
+    ck_valid = set(int(ck_slot[n]) for n in valid)
+    for n in valid:
+        ref[ck_slot[n]] = got[ck_slot[n]]  # compared below against the prefix runs
+    check_pages(g, got, ref, slots=list(idx), what=f"d={d} pages")
+    sub = dataclasses.replace(g, num_slots=1)
+    for n in valid:
+        want = oracle_prefix_page(img, inp, n, int(ck_len[n]))
+        page = got[ck_slot[n]][None].copy()
+        # the checkpoint page's padding must be the original bytes
+        pad = slice(g.conv_off + g.conv_region_bytes, g.page_stride)
+        assert np.array_equal(page[0, pad], img[ck_slot[n], pad])
+        want[0, pad] = page[0, pad]
+        check_pages(sub, page, want, what=f"d={d} checkpoint of sequence {n}")
+    assert len(ck_valid) == len(valid)
+
+
+def test_checkpoint_emission_full_size_equals_prefix_prefill():
+    """8 sequences, 16 heads x 128x128: each sequence emits its state at its
+    last 256-token block boundary; the checkpoint pages equal the pages a
+    separate prefill of those prefixes leaves, bit for bit, and the call's
+    outputs equal those of the plain prefill."""
+    inp, img = wl.prefill_workload(seed=0)
+    g = inp.geom
+    lens = np.diff(inp.cu_seqlens)
+    ck_len = (lens // 256 * 256).astype(np.int32)
+    spare = np.array([s for s in range(g.num_slots) if s not in set(inp.state_indices.tolist())],
+                     np.int32)
+    ck_slot = spare[:inp.num_seqs].copy()
+    log(f"full size: lengths {lens.tolist()}, checkpoints at {ck_len.tolist()}")
+    a = DevicePool(g, [img])
+    ta = step_tensors(inp)
+    assert gdn.gdn_prefill_varlen_checkpoint(a.pool, 0, inp.num_seqs, ta["cu"], inp.max_seqlen,
+                                             inp.total_tokens, args_of(ta, inp), to_dev(ck_slot),
+                                             to_dev(ck_len)) == gdn.GDN_OK
+    # the same call without checkpoints
+    b = DevicePool(g, [img])
+    tb = step_tensors(inp)
+    assert gdn.gdn_prefill_varlen(b.pool, 0, inp.num_seqs, tb["cu"], inp.max_seqlen,
+                                  inp.total_tokens, args_of(tb, inp)) == gdn.GDN_OK
+    # the prefixes alone, into the sequences' own slots of a third pool
+    sel = np.concatenate([np.arange(inp.cu_seqlens[n], inp.cu_seqlens[n] + ck_len[n])
+                          for n in range(inp.num_seqs)])
+    pre = dataclasses.replace(inp, x=inp.x[sel], alpha=inp.alpha[sel], beta=inp.beta[sel],
+                              cu_seqlens=np.concatenate([[0], np.cumsum(ck_len)]).astype(np.int32))
+    c = DevicePool(g, [img])
+    tc = step_tensors(pre)
+    assert gdn.gdn_prefill_varlen(c.pool, 0, pre.num_seqs, tc["cu"], pre.max_seqlen,
+                                  pre.total_tokens, args_of(tc, pre)) == gdn.GDN_OK
+    torch.cuda.synchronize()
+    assert torch.equal(ta["out"], tb["out"])
+    idx_t = torch.from_numpy(inp.state_indices.astype(np.int64)).cuda()
+    ck_t = torch.from_numpy(ck_slot.astype(np.int64)).cuda()
+    assert torch.equal(a.bufs[0][idx_t], b.bufs[0][idx_t])
+    pay = g.conv_off + g.conv_region_bytes
+    assert torch.equal(a.bufs[0][ck_t][:, :pay], c.bufs[0][idx_t][:, :pay])
+    assert torch.equal(a.bufs[0][ck_t][:, pay:], b.bufs[0][ck_t][:, pay:])  # padding as it was

@@ -172,9 +172,37 @@ def bench_restore(steps, warmup):
                max(1, warmup // 5), stream)
     hits = int((ops[:, 1] >= 0).sum())
     nbytes = 2 * hits * int(linear.sum()) * (g.ssm_region_bytes + g.conv_region_bytes)
+    snap = bench_snapshot(h, int(ops[0, 0]), int(ops[1, 0]),
+                          int(linear.sum()) * (g.ssm_region_bytes + g.conv_region_bytes))
     del bufs
     torch.cuda.empty_cache()
-    return ms, nbytes, hits, int(linear.sum())
+    return ms, nbytes, hits, int(linear.sum()), snap
+
+
+def bench_snapshot(pool, slot_a, slot_b, payload, reps=3):
+    """Save one slot (every GDN layer) to a snapshot file and load it into
+    another slot, host time including the device copies, CRC-32C and file I/O."""
+    import tempfile
+
+    import hybrid_linear_attention_slot_amd as gdn
+    d = tempfile.mkdtemp(prefix="gdn_snap_")
+    path = os.path.join(d, "slot.snap")
+    t_save = t_load = 0.0
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        gdn.gdn_snapshot_save(pool, slot_a, 1, 0, path)
+        t1 = time.perf_counter()
+        gdn.gdn_snapshot_load(pool, slot_b, path, 1)
+        t2 = time.perf_counter()
+        t_save += t1 - t0
+        t_load += t2 - t1
+    os.remove(path)
+    os.rmdir(d)
+    return {"payload_bytes": payload, "save_ms": round(t_save / reps * 1e3, 2),
+            "load_ms": round(t_load / reps * 1e3, 2),
+            "save_gb_per_s": round(payload / (t_save / reps) / 1e9, 3),
+            "load_gb_per_s": round(payload / (t_load / reps) / 1e9, 3),
+            "where": d.rsplit("/", 1)[0]}
 
 
 def bench_slot_manager(rows=256, steps=200):
@@ -280,10 +308,11 @@ def main():
                               "into a spare slot (gdn_prefill_varlen_checkpoint)"}
     restore = None
     if not a.no_restore:
-        rms, rbytes, hits, nlin = bench_restore(a.steps, a.warmup)
+        rms, rbytes, hits, nlin, snap = bench_restore(a.steps, a.warmup)
         restore = {"gb_per_s": round(rbytes / (rms * 1e-3) / 1e9, 2), "ms_per_call": round(rms, 4),
                    "bytes": rbytes, "hits": hits, "gdn_layers": nlin,
-                   "frac_of_hbm_peak": round(rbytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                   "frac_of_hbm_peak": round(rbytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "snapshot_one_slot": snap}
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),

@@ -25,10 +25,13 @@ GDN_EUNSUPPORTED = -5
 GDN_EHIP = -6
 GDN_ENOSLOT = -7
 GDN_ESTATE = -8
+GDN_EIO = -9
+GDN_ECORRUPT = -10
 
 ERROR_NAMES = {GDN_EINVAL: "GDN_EINVAL", GDN_ERANGE: "GDN_ERANGE", GDN_EOVERLAP: "GDN_EOVERLAP",
                GDN_EALIGN: "GDN_EALIGN", GDN_EUNSUPPORTED: "GDN_EUNSUPPORTED",
-               GDN_EHIP: "GDN_EHIP", GDN_ENOSLOT: "GDN_ENOSLOT", GDN_ESTATE: "GDN_ESTATE"}
+               GDN_EHIP: "GDN_EHIP", GDN_ENOSLOT: "GDN_ENOSLOT", GDN_ESTATE: "GDN_ESTATE",
+               GDN_EIO: "GDN_EIO", GDN_ECORRUPT: "GDN_ECORRUPT"}
 
 GDN_SLOT_FREE, GDN_SLOT_LIVE, GDN_SLOT_CHECKPOINT, GDN_SLOT_RESERVED = 0, 1, 2, 3
 
@@ -78,6 +81,15 @@ class gdn_linear_state_op(C.Structure):
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class gdn_snapshot_info(C.Structure):
+    _fields_ = [("key", C.c_uint64), ("position", C.c_int64), ("num_linear_layers", C.c_int32),
+                ("conv_channels", C.c_int32), ("conv_width", C.c_int32),
+                ("num_k_heads", C.c_int32), ("num_v_heads", C.c_int32),
+                ("head_k_dim", C.c_int32), ("head_v_dim", C.c_int32),
+                ("window_bytes", C.c_int64), ("state_bytes", C.c_int64),
+                ("payload_bytes", C.c_int64), ("payload_crc", C.c_uint32)]
 
 
 _lib = None
@@ -133,6 +145,14 @@ def lib() -> C.CDLL:
         L.gdn_slots_lookup.argtypes = [p, u64]
         L.gdn_slots_lookup.restype = i32
         L.gdn_slots_counts.argtypes = [p, C.POINTER(i32)]
+        L.gdn_crc32c.argtypes = [C.c_uint32, p, C.c_size_t]
+        L.gdn_crc32c.restype = C.c_uint32
+        L.gdn_snapshot_save.argtypes = [p, i32, u64, i64, C.c_char_p, p]
+        L.gdn_snapshot_save.restype = C.c_int
+        L.gdn_snapshot_load.argtypes = [p, i32, C.c_char_p, u64, C.POINTER(i64), i32, p]
+        L.gdn_snapshot_load.restype = C.c_int
+        L.gdn_snapshot_read_info.argtypes = [C.c_char_p, C.POINTER(gdn_snapshot_info)]
+        L.gdn_snapshot_read_info.restype = C.c_int
         for f in ("gdn_slots_create", "gdn_slots_add_sequence", "gdn_slots_remove_sequence",
                   "gdn_slots_resolve", "gdn_slots_commit", "gdn_slots_abort",
                   "gdn_slots_restore_ops", "gdn_slots_slot_info", "gdn_slots_sequence_info",
@@ -367,3 +387,32 @@ def gdn_slots_counts(m: SlotManager) -> list:
     c = (C.c_int32 * 4)()
     _check(lib().gdn_slots_counts(m.handle, c))
     return list(c)
+
+
+# ---------------------------------------------------------------------------
+# State snapshots on disk (include/gdn_snapshot.h)
+# ---------------------------------------------------------------------------
+def gdn_crc32c(data: bytes, crc: int = 0) -> int:
+    buf = C.create_string_buffer(bytes(data), len(data))
+    return int(lib().gdn_crc32c(crc, buf, len(data)))
+
+
+def gdn_snapshot_save(pool: Pool, slot: int, key: int, position: int, path: str,
+                      stream=None) -> None:
+    _check(lib().gdn_snapshot_save(pool.handle, slot, key, position, os.fsencode(path),
+                                   _stream(stream)))
+
+
+def gdn_snapshot_load(pool: Pool, slot: int, path: str, key: int, drop_damaged: bool = False,
+                      stream=None) -> int:
+    """Returns the stored position."""
+    pos = C.c_int64()
+    _check(lib().gdn_snapshot_load(pool.handle, slot, os.fsencode(path), key, C.byref(pos),
+                                   1 if drop_damaged else 0, _stream(stream)))
+    return pos.value
+
+
+def gdn_snapshot_read_info(path: str) -> dict:
+    info = gdn_snapshot_info()
+    _check(lib().gdn_snapshot_read_info(os.fsencode(path), C.byref(info)))
+    return {f: getattr(info, f) for f, _ in gdn_snapshot_info._fields_}

@@ -70,6 +70,17 @@ def test_prefill_matches_oracle(Hk, Hv, d, W):
     run_and_check(g, inp, img, "prefill", f"prefill d={d} W={W}")
 
 
+@pytest.mark.parametrize("Hk,Hv,d", [(1, 3, 32), (2, 8, 64), (1, 4, 128), (2, 6, 128)])
+def test_wider_gqa_groups_match_oracle(Hk, Hv, d):
+    """Three or four v-heads per k-head: the decode's head pairs then include
+    a second pair or a single head."""
+    g = wl.make_geometry(10, Hk=Hk, Hv=Hv, dk=d, dv=d, W=4, page_align=128, extra_pad=128)
+    inp, img = case(g, 400 + Hv + d, [1] * 6, [1, 0, 1, 1, 0, 1], bias=True)
+    run_and_check(g, inp, img, "decode", f"decode G={Hv // Hk} d={d}")
+    inp, img = case(g, 500 + Hv + d, [37, 16, 1, 50], [1, 0, 1, 0], bias=True)
+    run_and_check(g, inp, img, "prefill", f"prefill G={Hv // Hk} d={d}")
+
+
 def test_padding_rows_and_out_of_range_slots():
     g = wl.tiny_geometry(extra_pad=128)
     inp, img = case(g, 7, [1, 1, 1, 1], [1, 1, 0, 1], slots=[2, -1, 5, 8])

@@ -98,6 +98,32 @@ struct PrefillParams {
 __device__ __forceinline__ float lo_bf16(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
+// The sequence at dispatch position r when sequences are placed by length:
+// the first half of the positions takes the longest sequences (longest
+// first), the second half the shortest (shortest first).  Each XCD fills its
+// CUs in dispatch order, so the long sequences get a CU each and then share
+// it with the short ones, which finish early.  Ranks break ties by index; up
+// to 64 sequences (one per lane), identity beyond.
+__device__ __forceinline__ int seq_at_position(const int32_t* cu, int N, int r)
+{
+    if (N > 64 || N < 2)
+        return r;
+    const int half = (N + 1) / 2;
+    const int want = r < half ? r : N - 1 - (r - half);
+    const int m = threadIdx.x & 63;
+    int rank = -1;
+    if (m < N) {
+        const int lm = cu[m + 1] - cu[m];
+        rank = 0;
+        for (int j = 0; j < N; ++j) {
+            const int lj = cu[j + 1] - cu[j];
+            rank += (lj > lm || (lj == lm && j < m)) ? 1 : 0;
+        }
+    }
+    const uint64_t hit = __ballot(rank == want);
+    return __ffsll(static_cast<long long>(hit)) - 1;
+}
+
 template <int RING>
 __device__ __forceinline__ int ring_pos(int t) // t >= -RING
 {
@@ -120,16 +146,18 @@ void prefill_kernel(PrefillParams p)
     __shared__ __align__(8) float gab[RING][2];        // staged alpha, beta
     __shared__ __align__(16) float ob[2][CT][ISZ];     // outputs of a chunk (fp32)
 
-    // workgroup -> (k-head g, sequence n, v-head of the group, slice): the
-    // workgroups of one (n, g) read the same q/k inputs and share an XCD
+    // workgroup -> (k-head g, dispatch position of sequence n, v-head of the
+    // group, slice): the workgroups of one (n, g) read the same q/k inputs and
+    // share an XCD
     const int G = p.Hv / p.Hk;
     const int nblocks = p.num_seqs * p.Hv * Sh::NSL;
     const int id = xcd_contiguous_id(blockIdx.x, nblocks);
     const int per_g = p.num_seqs * G * Sh::NSL;
     const int g = id / per_g;
     const int r0 = id - g * per_g;
-    const int n = r0 / (G * Sh::NSL);
-    const int r1 = r0 - n * (G * Sh::NSL);
+    const int pos = r0 / (G * Sh::NSL);
+    const int n = __builtin_amdgcn_readfirstlane(seq_at_position(p.cu, p.num_seqs, pos));
+    const int r1 = r0 - pos * (G * Sh::NSL);
     const int h = g * G + r1 / Sh::NSL;
     const int sl = r1 % Sh::NSL;
 

@@ -81,6 +81,18 @@ def test_wider_gqa_groups_match_oracle(Hk, Hv, d):
     run_and_check(g, inp, img, "prefill", f"prefill G={Hv // Hk} d={d}")
 
 
+def test_prefill_many_short_sequences():
+    """More sequences than one wave can rank (the placement by length then
+    keeps the natural order), lengths 0..20 including many shorter than the
+    conv window."""
+    g = wl.make_geometry(96, Hk=2, Hv=4, dk=32, dv=32, W=4, page_align=128, extra_pad=128)
+    rng = wl.rng_for(77)
+    lens = rng.integers(0, 21, size=80)
+    warm = (rng.random(80) < 0.5).astype(np.uint8)
+    inp, img = case(g, 78, lens, warm, bias=True)
+    run_and_check(g, inp, img, "prefill", "prefill 80 short sequences")
+
+
 def test_padding_rows_and_out_of_range_slots():
     g = wl.tiny_geometry(extra_pad=128)
     inp, img = case(g, 7, [1, 1, 1, 1], [1, 1, 0, 1], slots=[2, -1, 5, 8])

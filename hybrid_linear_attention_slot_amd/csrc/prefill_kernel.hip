@@ -28,14 +28,16 @@
 // Consumers and producers meet at one barrier per chunk; the per-token work
 // on the critical path is the consumers' recurrence alone.  The L2 norm
 // factors are applied to the reduced sums, so k and q stay raw in LDS.
-// Every arithmetic step of a token is the same wherever the chunk boundaries
-// fall, so a run split at any token and resumed from the written-back state
-// gives the same bits as the straight run.
+// A run split at a multiple of the chunk length (16 tokens) and resumed from
+// the written-back state gives the same bits as the straight run: the state
+// is folded to its plain form at every chunk start, which is also the form
+// written back.
 //
 // The conv window is rewritten by a second small kernel after this one, so
 // that no workgroup of a sequence can overwrite the window another workgroup
 // of the same sequence has yet to read.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_utils.h"
 #include "gdn_internal.h"
@@ -68,6 +70,7 @@ struct PrefillShape {
     static_assert(DK == DV, "square heads only");
     static_assert(KPL % 4 == 0 && DK % KPL == 0 && LPC >= 1 && LPC <= 64, "key split");
     static_assert(NCONS >= 1 && DV % ISZ == 0 && ISZ % 8 == 0, "column split");
+    static_assert(CT == 16, "a chunk's decays are reduced over one 16-lane DPP row");
 };
 
 struct PrefillParams {
@@ -124,6 +127,10 @@ __device__ __forceinline__ int seq_at_position(const int32_t* cu, int N, int r)
     return __ffsll(static_cast<long long>(hit)) - 1;
 }
 
+// The scale of the state is folded into it once it falls below 2^-40 (bits
+// of the float), so s stays within 2^40 of the state's magnitude.
+constexpr uint32_t kFoldBelow = (127u - 40u) << 23;
+
 template <int RING>
 __device__ __forceinline__ int ring_pos(int t) // t >= -RING
 {
@@ -143,6 +150,7 @@ void prefill_kernel(PrefillParams p)
     __shared__ __align__(16) uint16_t raw[RING][NCH];  // staged raw inputs, row = token % RING
     __shared__ __align__(16) float ys[2][CT][NCH];     // conv outputs (raw q | raw k | v)
     __shared__ __align__(16) float sc[2][CT][8];       // a, b, rk, rq, k^.q^ per token
+                                                       // (+ the chunk's no-fold flag)
     __shared__ __align__(8) float gab[RING][2];        // staged alpha, beta
     __shared__ __align__(16) float ob[2][CT][ISZ];     // outputs of a chunk (fp32)
 
@@ -222,7 +230,28 @@ void prefill_kernel(PrefillParams p)
             r.kq = sc[buf][tt][4];
             r.v = yt[2 * DK + col];
         };
-        auto step = [&](const Ops& r, int buf, int tt) {
+        // The state is held as cs * s: the decays of a chunk's tokens gather in
+        // the lane-uniform scale cs, so a token's update is one fma per
+        // element.  The scale is folded back into s at the start of every
+        // chunk, and at once should it fall below kFoldBelow.
+        float cs = 1.f;
+        auto fold = [&](float c) {
+#pragma unroll
+            for (int m = 0; m < KPL; ++m)
+                s[m] *= c;
+        };
+        // `checked`: whether the scale may have to be folded within the chunk
+        // (the producers rule it out for most chunks)
+        auto step = [&](const Ops& r, int buf, int tt, auto checked) {
+            const float a = r.g.x, b = r.g.y, rk = r.g.z, rq = r.g.w;
+            float ca = cs * a; // a S_old = ca s
+            if constexpr (decltype(checked)::value) {
+                if ((__builtin_amdgcn_readfirstlane(__float_as_uint(ca)) & 0x7FFFFFFFu) <
+                    kFoldBelow) {
+                    fold(ca);
+                    ca = 1.f;
+                }
+            }
             float u0 = 0.f, u1 = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
             for (int m = 0; m < KPL / 4; ++m) {
@@ -235,19 +264,20 @@ void prefill_kernel(PrefillParams p)
                 o0 = fmaf(s[4 * m + 2], r.q[m].z, o0);
                 o1 = fmaf(s[4 * m + 3], r.q[m].w, o1);
             }
-            const float u = group_sum<LPC>(u0 + u1); // S_old k (raw k)
-            const float o = group_sum<LPC>(o0 + o1); // S_old q (raw q)
-            const float a = r.g.x, b = r.g.y, rk = r.g.z, rq = r.g.w;
-            const float d = b * (r.v - (a * rk) * u); // b (v - a S_old k^)
-            const float dk = d * rk;                  // S <- a S + d k^T, k^ = rk k
+            const float u = group_sum<LPC>(u0 + u1); // s k (raw k)
+            const float o = group_sum<LPC>(o0 + o1); // s q (raw q)
+            const float d = b * (r.v - (ca * rk) * u); // b (v - a S_old k^)
+            // S <- a S_old + d k^ k^T = ca (s + (d rk / ca) k)
+            const float dk = d * (rk * __builtin_amdgcn_rcpf(ca));
 #pragma unroll
             for (int m = 0; m < KPL / 4; ++m) {
-                s[4 * m + 0] = fmaf(dk, r.k[m].x, a * s[4 * m + 0]);
-                s[4 * m + 1] = fmaf(dk, r.k[m].y, a * s[4 * m + 1]);
-                s[4 * m + 2] = fmaf(dk, r.k[m].z, a * s[4 * m + 2]);
-                s[4 * m + 3] = fmaf(dk, r.k[m].w, a * s[4 * m + 3]);
+                s[4 * m + 0] = fmaf(dk, r.k[m].x, s[4 * m + 0]);
+                s[4 * m + 1] = fmaf(dk, r.k[m].y, s[4 * m + 1]);
+                s[4 * m + 2] = fmaf(dk, r.k[m].z, s[4 * m + 2]);
+                s[4 * m + 3] = fmaf(dk, r.k[m].w, s[4 * m + 3]);
             }
-            const float ov = fmaf(a * rq, o, r.kq * d); // a S_old q^ + d (k^.q^)
+            cs = ca;
+            const float ov = fmaf(ca * rq, o, r.kq * d); // a S_old q^ + d (k^.q^)
             if (jl == 0)
                 ob[buf][tt][col] = ov;
         };
@@ -274,7 +304,7 @@ void prefill_kernel(PrefillParams p)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     __builtin_amdgcn_raw_buffer_store_b32(
-                        __float_as_uint(s[4 * m + e]), ck_rs,
+                        __float_as_uint(s[4 * m + e] * cs), ck_rs,
                         voff + (4 * LPC * m + e) * DV * 4, 0, 0);
         };
         __syncthreads(); // A: history and chunk 0 staged
@@ -282,25 +312,34 @@ void prefill_kernel(PrefillParams p)
         for (int c = 0; c < nchunks; ++c) {
             const int buf = c & 1;
             const int nt = chunk_len(c);
+            fold(cs);
+            cs = 1.f;
+            // the producers' verdict: no token of the chunk needs a fold
+            const bool nofold = __builtin_amdgcn_readfirstlane(__float_as_uint(sc[buf][0][5])) != 0u;
             Ops A, B;
-            if (nt == CT && ck_tok / CT != c) {
+            auto per_token = [&](auto checked) {
+                for (int tt = 0; tt < nt; ++tt) {
+                    fetch(A, buf, tt);
+                    step(A, buf, tt, checked);
+                    if (c * CT + tt == ck_tok)
+                        store_ck();
+                }
+            };
+            if (nt == CT && ck_tok / CT != c && nofold) {
                 // full chunk: a fixed-trip loop without branches, so that each
                 // token waits only for its own operands (the last fetch of the
                 // chunk re-reads token CT-1 and is unused)
                 fetch(A, buf, 0);
                 for (int tt = 0; tt < CT; tt += 2) {
                     fetch(B, buf, tt + 1);
-                    step(A, buf, tt);
+                    step(A, buf, tt, std::false_type{});
                     fetch(A, buf, min(tt + 2, CT - 1));
-                    step(B, buf, tt + 1);
+                    step(B, buf, tt + 1, std::false_type{});
                 }
-            } else { // a ragged last chunk, or the chunk holding the checkpoint token
-                for (int tt = 0; tt < nt; ++tt) {
-                    fetch(A, buf, tt);
-                    step(A, buf, tt);
-                    if (c * CT + tt == ck_tok)
-                        store_ck();
-                }
+            } else if (nofold) { // a ragged last chunk, or the chunk holding the checkpoint token
+                per_token(std::false_type{});
+            } else {
+                per_token(std::true_type{});
             }
             __syncthreads();
         }
@@ -308,7 +347,7 @@ void prefill_kernel(PrefillParams p)
         for (int m = 0; m < KPL / 4; ++m)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                tile[(4 * jl + 4 * LPC * m + e) * DV + gcol] = s[4 * m + e];
+                tile[(4 * jl + 4 * LPC * m + e) * DV + gcol] = s[4 * m + e] * cs;
         return;
     }
 
@@ -349,7 +388,10 @@ void prefill_kernel(PrefillParams p)
     // Every lane issues the same number of 16-byte loads whatever the chunk's
     // length (pieces past the last token re-read the last token's row and land
     // in ring rows no conv reads), so the waits for them are exact.
-    uint4 pf[Sh::LOADS];
+    // (a native vector type: an array of HIP's uint4 is kept in scratch memory
+    // here, which turns the prefetch into a load, a wait and a spill)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 pf[Sh::LOADS];
     float2 pg;
     auto issue = [&](int k) {
         if (k >= nchunks)
@@ -359,7 +401,7 @@ void prefill_kernel(PrefillParams p)
         for (int i = 0; i < Sh::LOADS; ++i) {
             const int e = min(plane + PLANES * i, CT * NPIECE - 1);
             const int tt = e / NPIECE, pc = e - tt * NPIECE;
-            pf[i] = *reinterpret_cast<const uint4*>(p.x + int64_t(tb + k * CT + min(tt, last)) * p.C +
+            pf[i] = *reinterpret_cast<const u32x4*>(p.x + int64_t(tb + k * CT + min(tt, last)) * p.C +
                                                    chan(8 * pc));
         }
         const int64_t gi = int64_t(tb + k * CT + min(plane % CT, last)) * p.Hv + h;
@@ -373,7 +415,7 @@ void prefill_kernel(PrefillParams p)
             const int e = plane + PLANES * i;
             if (e < CT * NPIECE) {
                 const int tt = e / NPIECE, pc = e - tt * NPIECE;
-                *reinterpret_cast<uint4*>(&raw[ring_pos<RING>(k * CT + tt)][8 * pc]) = pf[i];
+                *reinterpret_cast<u32x4*>(&raw[ring_pos<RING>(k * CT + tt)][8 * pc]) = pf[i];
             }
         }
         if (plane < CT)
@@ -480,6 +522,22 @@ void prefill_kernel(PrefillParams p)
                 my_sk = tk;
                 my_qk = tx;
             }
+        }
+        if (pw == 0) {
+            // whether the state's scale can stay unfolded through the chunk:
+            // every decay in [0, 1] and their product at least 2^-40, so that
+            // no running product falls below it (NaN fails the tests)
+            const int nt = chunk_len(k);
+            const float av = lane < nt ? gab[base + lane][0] : 1.f;
+            const bool ok = av >= 0.f && av <= 1.f;
+            float pr = av; // product over lanes 0..15 (one DPP row)
+            pr *= dpp_mov<kDppQuadXor1>(pr);
+            pr *= dpp_mov<kDppQuadXor2>(pr);
+            pr *= dpp_mov<kDppRowHalfMirror>(pr);
+            pr *= dpp_mov<kDppRowMirror>(pr);
+            const bool all_ok = __ballot(!ok) == 0;
+            if (lane == 0)
+                sc[buf][0][5] = (all_ok && pr >= __uint_as_float(kFoldBelow)) ? 1.f : 0.f;
         }
         const int tt = t0 + lane;
         if (lane < TPW && tt < t1) {

@@ -81,6 +81,56 @@ def test_wider_gqa_groups_match_oracle(Hk, Hv, d):
     run_and_check(g, inp, img, "prefill", f"prefill G={Hv // Hk} d={d}")
 
 
+def extreme_decays(rng, T, Hv):
+    """Decays that drive the running product of a chunk below 2^-40: runs of
+    0.02 (below it after 8 tokens), exact zeros, 1e-30 and a subnormal, exact
+    ones, mixed with the ordinary draw."""
+    a = np.exp(-np.logaddexp(0.0, rng.standard_normal((T, Hv)))).astype(np.float32)
+    kind = rng.integers(0, 6, size=(T, Hv))
+    a[kind == 1] = 0.02
+    a[(kind == 2) & (rng.random((T, Hv)) < 0.1)] = 0.0
+    a[(kind == 3) & (rng.random((T, Hv)) < 0.1)] = 1e-30
+    a[(kind == 3) & (rng.random((T, Hv)) < 0.05)] = np.float32(1e-40)
+    a[kind == 4] = 1.0
+    a[:, 0] = 0.02  # one head decays at 0.02 throughout
+    return a
+
+
+@pytest.mark.parametrize("d", [32, 128])
+def test_prefill_extreme_decays_match_oracle(d):
+    """The prefill keeps the state as a scale times a matrix and folds the
+    scale in when it gets small; decays of 0, 1e-30, subnormals and long runs
+    of 0.02 must still give the oracle's results, and a split at token 32
+    (a chunk boundary) the straight run's bits."""
+    g = wl.make_geometry(16, Hk=2, Hv=4, dk=d, dv=d, W=4, page_align=128, extra_pad=128)
+    lens = [64, 64, 41, 17]
+    inp, img = case(g, 900 + d, lens, [1, 0, 1, 0], bias=True)
+    rng = wl.rng_for(901 + d)
+    inp.alpha = extreme_decays(rng, inp.total_tokens, g.Hv)
+    run_and_check(g, inp, img, "prefill", f"extreme decays d={d}")
+    # straight 64 tokens vs 32 + 32 on the first two sequences
+    two = dataclasses.replace(inp, x=inp.x[:128], alpha=inp.alpha[:128], beta=inp.beta[:128],
+                              cu_seqlens=np.array([0, 64, 128], np.int32),
+                              state_indices=inp.state_indices[:2],
+                              has_initial_state=inp.has_initial_state[:2])
+    sel = [np.r_[0:32, 64:96], np.r_[32:64, 96:128]]
+    halves = [dataclasses.replace(two, x=two.x[s], alpha=two.alpha[s], beta=two.beta[s],
+                                  cu_seqlens=np.array([0, 32, 64], np.int32),
+                                  has_initial_state=two.has_initial_state if i == 0 else
+                                  np.ones(2, np.uint8))
+              for i, s in enumerate(sel)]
+    a = DevicePool(g, [img])
+    t_s = run_prefill(a, 0, two)
+    b = DevicePool(g, [img])
+    run_prefill(b, 0, halves[0])
+    t_2 = run_prefill(b, 0, halves[1])
+    torch.cuda.synchronize()
+    o_s = u16(t_s["out"]).reshape(2, 64, g.Hv, g.dv)
+    o_2 = u16(t_2["out"]).reshape(2, 32, g.Hv, g.dv)
+    assert np.array_equal(o_2, o_s[:, 32:]), "split run differs from the straight run"
+    assert np.array_equal(a.host(), b.host()), "split run's pages differ"
+
+
 def test_prefill_many_short_sequences():
     """More sequences than one wave can rank (the placement by length then
     keeps the natural order), lengths 0..20 including many shorter than the

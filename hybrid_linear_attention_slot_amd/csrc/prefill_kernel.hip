@@ -62,7 +62,6 @@ struct PrefillShape {
     static constexpr int QKP = DK / 2;                              // q (and k) channel pairs
     static constexpr int NQK = (QKP + 63) / 64;                     // q/k pair slots per lane
     static constexpr int NVP = ISZ / 2;                             // v channel pairs
-    static constexpr int NVS = (NVP + 63) / 64;                     // v pair slots per lane
     static constexpr int PLANES = 64 * NPROD;
     static constexpr int LOADS = (CT * NPIECE + PLANES - 1) / PLANES; // pieces per producer lane
     static constexpr int OPR = ISZ / 8;                             // 8-column output pieces per row
@@ -131,6 +130,22 @@ __device__ __forceinline__ int seq_at_position(const int32_t* cu, int N, int r)
 // of the float), so s stays within 2^40 of the state's magnitude.
 constexpr uint32_t kFoldBelow = (127u - 40u) << 23;
 
+// A token's coefficients in LDS (floats):
+//   SC_SCALED  c rk, b, rk / c, c rq   (c: running product of the chunk's
+//                                      decays through the token)
+//   SC_KQ      k^.q^, c
+//   SC_PLAIN   a, b, rk, rq            (chunks that may need a fold)
+constexpr int SC_SCALED = 0, SC_KQ = 4, SC_PLAIN = 8;
+
+// v * (lane v of the row n lanes lower), or v * 1 for the first n lanes of
+// each 16-lane row (DPP row_shr; an invalid source keeps the `old` operand)
+template <int N>
+__device__ __forceinline__ float row_shr_or_one(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(v),
+                                                      0x110 + N, 0xF, 0xF, false));
+}
+
 template <int RING>
 __device__ __forceinline__ int ring_pos(int t) // t >= -RING
 {
@@ -149,8 +164,8 @@ void prefill_kernel(PrefillParams p)
 
     __shared__ __align__(16) uint16_t raw[RING][NCH];  // staged raw inputs, row = token % RING
     __shared__ __align__(16) float ys[2][CT][NCH];     // conv outputs (raw q | raw k | v)
-    __shared__ __align__(16) float sc[2][CT][8];       // a, b, rk, rq, k^.q^ per token
-                                                       // (+ the chunk's no-fold flag)
+    __shared__ __align__(16) float sc[2][CT][12];      // per token coefficients (SC_*)
+    __shared__ uint32_t nofold[2];                     // the chunk's decays need no fold
     __shared__ __align__(8) float gab[RING][2];        // staged alpha, beta
     __shared__ __align__(16) float ob[2][CT][ISZ];     // outputs of a chunk (fp32)
 
@@ -216,18 +231,20 @@ void prefill_kernel(PrefillParams p)
         // the current one is computed
         struct Ops {
             float4 k[KPL / 4], q[KPL / 4];
-            float4 g; // a, b, rk, rq
-            float kq, v;
+            float4 g; // SC_SCALED or SC_PLAIN
+            float2 h; // k^.q^, running scale
+            float v;
         };
-        auto fetch = [&](Ops& r, int buf, int tt) {
+        auto fetch = [&](Ops& r, int buf, int tt, auto checked) {
             const float* yt = ys[buf][tt];
 #pragma unroll
             for (int m = 0; m < KPL / 4; ++m) {
                 r.k[m] = *reinterpret_cast<const float4*>(yt + DK + 4 * jl + 4 * LPC * m);
                 r.q[m] = *reinterpret_cast<const float4*>(yt + 4 * jl + 4 * LPC * m);
             }
-            r.g = *reinterpret_cast<const float4*>(sc[buf][tt]);
-            r.kq = sc[buf][tt][4];
+            r.g = *reinterpret_cast<const float4*>(
+                &sc[buf][tt][decltype(checked)::value ? SC_PLAIN : SC_SCALED]);
+            r.h = *reinterpret_cast<const float2*>(&sc[buf][tt][SC_KQ]);
             r.v = yt[2 * DK + col];
         };
         // The state is held as cs * s: the decays of a chunk's tokens gather in
@@ -240,17 +257,29 @@ void prefill_kernel(PrefillParams p)
             for (int m = 0; m < KPL; ++m)
                 s[m] *= c;
         };
-        // `checked`: whether the scale may have to be folded within the chunk
-        // (the producers rule it out for most chunks)
+        // `checked`: whether the scale may have to be folded within the chunk.
+        // The producers rule that out for most chunks; the scale after each of
+        // their tokens is then the running product of the chunk's decays,
+        // which they also fold into the token's coefficients.
         auto step = [&](const Ops& r, int buf, int tt, auto checked) {
-            const float a = r.g.x, b = r.g.y, rk = r.g.z, rq = r.g.w;
-            float ca = cs * a; // a S_old = ca s
-            if constexpr (decltype(checked)::value) {
+            constexpr bool kChecked = decltype(checked)::value;
+            const float b = r.g.y, kq = r.h.x;
+            float ca, cu, rkc, cq; // a S_old = ca s; ca rk; rk / ca; ca rq
+            if constexpr (kChecked) {
+                ca = cs * r.g.x;
                 if ((__builtin_amdgcn_readfirstlane(__float_as_uint(ca)) & 0x7FFFFFFFu) <
                     kFoldBelow) {
                     fold(ca);
                     ca = 1.f;
                 }
+                cu = ca * r.g.z;
+                rkc = r.g.z * __builtin_amdgcn_rcpf(ca);
+                cq = ca * r.g.w;
+            } else {
+                ca = r.h.y;
+                cu = r.g.x;
+                rkc = r.g.z;
+                cq = r.g.w;
             }
             float u0 = 0.f, u1 = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
@@ -266,9 +295,9 @@ void prefill_kernel(PrefillParams p)
             }
             const float u = group_sum<LPC>(u0 + u1); // s k (raw k)
             const float o = group_sum<LPC>(o0 + o1); // s q (raw q)
-            const float d = b * (r.v - (ca * rk) * u); // b (v - a S_old k^)
+            const float d = b * (r.v - cu * u); // b (v - a S_old k^)
             // S <- a S_old + d k^ k^T = ca (s + (d rk / ca) k)
-            const float dk = d * (rk * __builtin_amdgcn_rcpf(ca));
+            const float dk = d * rkc;
 #pragma unroll
             for (int m = 0; m < KPL / 4; ++m) {
                 s[4 * m + 0] = fmaf(dk, r.k[m].x, s[4 * m + 0]);
@@ -277,9 +306,11 @@ void prefill_kernel(PrefillParams p)
                 s[4 * m + 3] = fmaf(dk, r.k[m].w, s[4 * m + 3]);
             }
             cs = ca;
-            const float ov = fmaf(ca * rq, o, r.kq * d); // a S_old q^ + d (k^.q^)
-            if (jl == 0)
-                ob[buf][tt][col] = ov;
+            // a S_old q^ + d (k^.q^); the LPC lanes of the column hold the same
+            // bits (each step of group_sum adds the same two values in every
+            // lane), so all of them store it: no exec-mask switch per token
+            const float ov = fmaf(cq, o, kq * d);
+            ob[buf][tt][col] = ov;
         };
         // checkpoint emission: the state after token ck_tok (if any) is also
         // stored into the checkpoint page
@@ -315,28 +346,29 @@ void prefill_kernel(PrefillParams p)
             fold(cs);
             cs = 1.f;
             // the producers' verdict: no token of the chunk needs a fold
-            const bool nofold = __builtin_amdgcn_readfirstlane(__float_as_uint(sc[buf][0][5])) != 0u;
+            const bool quiet = __builtin_amdgcn_readfirstlane(nofold[buf]) != 0u;
             Ops A, B;
             auto per_token = [&](auto checked) {
                 for (int tt = 0; tt < nt; ++tt) {
-                    fetch(A, buf, tt);
+                    fetch(A, buf, tt, checked);
                     step(A, buf, tt, checked);
                     if (c * CT + tt == ck_tok)
                         store_ck();
                 }
             };
-            if (nt == CT && ck_tok / CT != c && nofold) {
+            if (nt == CT && ck_tok / CT != c && quiet) {
                 // full chunk: a fixed-trip loop without branches, so that each
                 // token waits only for its own operands (the last fetch of the
                 // chunk re-reads token CT-1 and is unused)
-                fetch(A, buf, 0);
+                constexpr std::false_type scaled{};
+                fetch(A, buf, 0, scaled);
                 for (int tt = 0; tt < CT; tt += 2) {
-                    fetch(B, buf, tt + 1);
-                    step(A, buf, tt, std::false_type{});
-                    fetch(A, buf, min(tt + 2, CT - 1));
-                    step(B, buf, tt + 1, std::false_type{});
+                    fetch(B, buf, tt + 1, scaled);
+                    step(A, buf, tt, scaled);
+                    fetch(A, buf, min(tt + 2, CT - 1), scaled);
+                    step(B, buf, tt + 1, scaled);
                 }
-            } else if (nofold) { // a ragged last chunk, or the chunk holding the checkpoint token
+            } else if (quiet) { // a ragged last chunk, or the chunk holding the checkpoint token
                 per_token(std::false_type{});
             } else {
                 per_token(std::true_type{});
@@ -356,9 +388,11 @@ void prefill_kernel(PrefillParams p)
     const int plane = pw * 64 + lane;
     const uint16_t* win = reinterpret_cast<const uint16_t*>(page + p.conv_off);
 
-    // conv taps and bias of the lane's channel pairs
-    float wq[Sh::NQK][2][W], wk[Sh::NQK][2][W], wv[Sh::NVS][2][W];
-    float bq[Sh::NQK][2], bk[Sh::NQK][2], bv[Sh::NVS][2];
+    // conv taps and bias of the lane's channel pairs: q and k pair `lane`
+    // (lanes past DK/2 idle), v pair `lane % NVP` of the slice
+    static_assert(Sh::NQK == 1 && 64 % Sh::NVP == 0, "one q/k pair per lane; v pairs tile a wave");
+    float wq[2][W], wk[2][W], wv[2][W];
+    float bq[2], bk[2], bv[2];
     auto load_taps = [&](int ch, float (&w2)[2][W], float (&b2)[2]) {
         const int c = chan(ch);
 #pragma unroll
@@ -369,20 +403,11 @@ void prefill_kernel(PrefillParams p)
             b2[i] = p.conv_b ? bf16_to_f32(p.conv_b[c + i]) : 0.f;
         }
     };
-#pragma unroll
-    for (int s = 0; s < Sh::NQK; ++s) {
-        const int pp = lane + 64 * s;
-        if (pp < QKP) {
-            load_taps(2 * pp, wq[s], bq[s]);
-            load_taps(DK + 2 * pp, wk[s], bk[s]);
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < Sh::NVS; ++s) {
-        const int pp = lane + 64 * s;
-        if (pp < Sh::NVP)
-            load_taps(2 * DK + 2 * pp, wv[s], bv[s]);
-    }
+    const int qkp = min(lane, QKP - 1); // q/k pair of the lane (clamped; idle lanes recompute)
+    const int vp = lane % Sh::NVP;      // v pair of the lane
+    load_taps(2 * qkp, wq, bq);
+    load_taps(DK + 2 * qkp, wk, bk);
+    load_taps(2 * DK + 2 * vp, wv, bv);
 
     // chunk k's raw rows and gates: issue (into registers), then stage (to LDS).
     // Every lane issues the same number of 16-byte loads whatever the chunk's
@@ -423,14 +448,17 @@ void prefill_kernel(PrefillParams p)
     };
 
     // conv + SiLU and the norm factors of chunk k into ys[k & 1], sc[k & 1].
-    // Producer wave pw takes the TPW consecutive tokens starting at pw * TPW;
-    // each lane walks them in order for its channel pairs, keeping the W-1
-    // previous inputs of each channel in registers (primed from the ring), so
-    // every staged input is unpacked once.  The wave sums of |q|^2, |k|^2 and
-    // q.k of the tokens are formed together at the end, and lane i finishes
-    // the norm factors of the wave's i-th token.
+    // Producer wave pw takes the TPW consecutive tokens starting at pw * TPW.
+    // For q and k each lane walks them in order for its channel pair, keeping
+    // the W-1 previous inputs in registers (primed from the ring), so every
+    // staged input is unpacked once; the v channels of the slice are fewer
+    // than the lanes, so there a lane takes one (token, pair) job and reads
+    // its window from the ring.  The 3 TPW wave sums (|q|^2, |k|^2, q.k of
+    // each token) are reduced together, and lane i finishes the coefficients
+    // of the wave's i-th token.
     auto prepare = [&](int k) {
         constexpr int TPW = Sh::TPW;
+        static_assert(TPW == 4, "the sums of 4 tokens are reduced together");
         const int buf = k & 1;
         const int t0 = pw * TPW;
         const int t1 = min(t0 + TPW, chunk_len(k));
@@ -441,25 +469,33 @@ void prefill_kernel(PrefillParams p)
             const int r = base + tt;
             return reinterpret_cast<const uint32_t*>(raw[r < 0 ? r + RING : r]);
         };
-        float hq[Sh::NQK][2][W - 1], hk[Sh::NQK][2][W - 1], hv[Sh::NVS][2][W - 1];
+        // v: job j = lane + 64 jj is token t0 + j / NVP, pair vp
+#pragma unroll
+        for (int jj = 0; jj < (TPW * Sh::NVP + 63) / 64; ++jj) {
+            const int i = (lane + 64 * jj) / Sh::NVP;
+            const int tt = t0 + i;
+            if (i < TPW && tt < t1) {
+                float a0 = bv[0], a1 = bv[1];
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    const uint32_t xv = row(tt - (W - 1) + w)[2 * QKP + vp];
+                    a0 = fmaf(wv[0][w], lo_bf16(xv), a0);
+                    a1 = fmaf(wv[1][w], hi_bf16(xv), a1);
+                }
+                *reinterpret_cast<float2*>(ys[buf][tt] + 2 * DK + 2 * vp) =
+                    make_float2(silu(a0), silu(a1));
+            }
+        }
+        // q, k
+        float hq[2][W - 1], hk[2][W - 1];
 #pragma unroll
         for (int w = 0; w < W - 1; ++w) {
             const uint32_t* r = row(t0 - (W - 1) + w);
-#pragma unroll
-            for (int s = 0; s < Sh::NQK; ++s) {
-                const int pp = min(lane + 64 * s, QKP - 1);
-                const uint32_t xq = r[pp], xk = r[QKP + pp];
-                hq[s][0][w] = lo_bf16(xq);
-                hq[s][1][w] = hi_bf16(xq);
-                hk[s][0][w] = lo_bf16(xk);
-                hk[s][1][w] = hi_bf16(xk);
-            }
-#pragma unroll
-            for (int s = 0; s < Sh::NVS; ++s) {
-                const uint32_t xv = r[2 * QKP + min(lane + 64 * s, Sh::NVP - 1)];
-                hv[s][0][w] = lo_bf16(xv);
-                hv[s][1][w] = hi_bf16(xv);
-            }
+            const uint32_t xq = r[qkp], xk = r[QKP + qkp];
+            hq[0][w] = lo_bf16(xq);
+            hq[1][w] = hi_bf16(xq);
+            hk[0][w] = lo_bf16(xk);
+            hk[1][w] = hi_bf16(xk);
         }
         // conv of one channel: taps over the W-1 held inputs and the current one,
         // then the held inputs shift by one
@@ -484,68 +520,68 @@ void prefill_kernel(PrefillParams p)
                 break;
             const uint32_t* r = row(tt);
             float* yt = ys[buf][tt];
-#pragma unroll
-            for (int s = 0; s < Sh::NQK; ++s) {
-                const int pp = lane + 64 * s;
-                const int pc = min(pp, QKP - 1);
-                const uint32_t xq = r[pc], xk = r[QKP + pc];
-                const float q0 = conv1(wq[s][0], bq[s][0], hq[s][0], lo_bf16(xq));
-                const float q1 = conv1(wq[s][1], bq[s][1], hq[s][1], hi_bf16(xq));
-                const float k0 = conv1(wk[s][0], bk[s][0], hk[s][0], lo_bf16(xk));
-                const float k1 = conv1(wk[s][1], bk[s][1], hk[s][1], hi_bf16(xk));
-                if (pp < QKP) {
-                    *reinterpret_cast<float2*>(yt + 2 * pp) = make_float2(q0, q1);
-                    *reinterpret_cast<float2*>(yt + DK + 2 * pp) = make_float2(k0, k1);
-                    sq[i] = fmaf(q0, q0, q1 * q1);
-                    sk[i] = fmaf(k0, k0, k1 * k1);
-                    qk[i] = fmaf(q0, k0, q1 * k1);
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < Sh::NVS; ++s) {
-                const int pp = lane + 64 * s;
-                const uint32_t xv = r[2 * QKP + min(pp, Sh::NVP - 1)];
-                const float v0 = conv1(wv[s][0], bv[s][0], hv[s][0], lo_bf16(xv));
-                const float v1 = conv1(wv[s][1], bv[s][1], hv[s][1], hi_bf16(xv));
-                if (pp < Sh::NVP)
-                    *reinterpret_cast<float2*>(yt + 2 * DK + 2 * pp) = make_float2(v0, v1);
+            const uint32_t xq = r[qkp], xk = r[QKP + qkp];
+            const float q0 = conv1(wq[0], bq[0], hq[0], lo_bf16(xq));
+            const float q1 = conv1(wq[1], bq[1], hq[1], hi_bf16(xq));
+            const float k0 = conv1(wk[0], bk[0], hk[0], lo_bf16(xk));
+            const float k1 = conv1(wk[1], bk[1], hk[1], hi_bf16(xk));
+            if (lane < QKP) {
+                *reinterpret_cast<float2*>(yt + 2 * lane) = make_float2(q0, q1);
+                *reinterpret_cast<float2*>(yt + DK + 2 * lane) = make_float2(k0, k1);
+                sq[i] = fmaf(q0, q0, q1 * q1);
+                sk[i] = fmaf(k0, k0, k1 * k1);
+                qk[i] = fmaf(q0, k0, q1 * k1);
             }
         }
-        float my_sq = 0.f, my_sk = 0.f, my_qk = 0.f;
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            if (t0 + i >= t1)
-                break;
-            const float tq = wave_total(sq[i]), tk = wave_total(sk[i]), tx = wave_total(qk[i]);
-            if (lane == i) {
-                my_sq = tq;
-                my_sk = tk;
-                my_qk = tx;
-            }
-        }
+        // wave sums: halves (tokens 0|1 and 2|3 share a register), then rows
+        // (row j then holds token (0, 2, 1, 3)[j]), then within the rows
+        auto fold_halves = [](float a, float b) { // lanes 0-31: a, lanes 32-63: b
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b),
+                                                           false, false);
+            return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        };
+        auto fold_rows = [](float x, float y) { // rows: x0+x1, y0+y1, x2+x3, y2+y3
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y),
+                                                           false, false);
+            return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        };
+        auto token_sums = [&](const float (&v)[TPW]) {
+            return group_sum<16>(fold_rows(fold_halves(v[0], v[1]), fold_halves(v[2], v[3])));
+        };
+        const float tsq = token_sums(sq), tsk = token_sums(sk), tqk = token_sums(qk);
+        const int src = 16 * (((lane & 1) << 1) | ((lane >> 1) & 1)); // row of token lane & 3
+        const float my_sq = __shfl(tsq, src, 64), my_sk = __shfl(tsk, src, 64),
+                    my_qk = __shfl(tqk, src, 64);
+        // running products of the chunk's decays: an inclusive scan over lanes
+        // 0..15 (one DPP row; lanes past the chunk's end take 1).  Whether the
+        // state's scale can stay unfolded through the chunk: every decay in
+        // [0, 1] and their product at least 2^-40, so that no running product
+        // falls below it (NaN fails the test).
+        const int ntk = chunk_len(k);
+        const float av = lane < ntk ? gab[base + lane][0] : 1.f;
+        float cp = av;
+        cp *= row_shr_or_one<1>(cp);
+        cp *= row_shr_or_one<2>(cp);
+        cp *= row_shr_or_one<4>(cp);
+        cp *= row_shr_or_one<8>(cp);
         if (pw == 0) {
-            // whether the state's scale can stay unfolded through the chunk:
-            // every decay in [0, 1] and their product at least 2^-40, so that
-            // no running product falls below it (NaN fails the tests)
-            const int nt = chunk_len(k);
-            const float av = lane < nt ? gab[base + lane][0] : 1.f;
             const bool ok = av >= 0.f && av <= 1.f;
-            float pr = av; // product over lanes 0..15 (one DPP row)
-            pr *= dpp_mov<kDppQuadXor1>(pr);
-            pr *= dpp_mov<kDppQuadXor2>(pr);
-            pr *= dpp_mov<kDppRowHalfMirror>(pr);
-            pr *= dpp_mov<kDppRowMirror>(pr);
-            const bool all_ok = __ballot(!ok) == 0;
+            const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cp), 15));
+            const bool quiet = __ballot(!ok) == 0 && total >= __uint_as_float(kFoldBelow);
             if (lane == 0)
-                sc[buf][0][5] = (all_ok && pr >= __uint_as_float(kFoldBelow)) ? 1.f : 0.f;
+                nofold[buf] = quiet ? 1u : 0u;
         }
+        const float ct = __shfl(cp, min(t0 + lane, 15), 64); // running product through token t0+lane
         const int tt = t0 + lane;
         if (lane < TPW && tt < t1) {
             const float rq = p.scale / sqrtf(my_sq + p.eps);
             const float rk = 1.0f / sqrtf(my_sk + p.eps);
             const float2 ab = *reinterpret_cast<const float2*>(gab[base + tt]);
-            *reinterpret_cast<float4*>(sc[buf][tt]) = make_float4(ab.x, ab.y, rk, rq);
-            sc[buf][tt][4] = my_qk * rq * rk;
+            float* o = sc[buf][tt];
+            *reinterpret_cast<float4*>(o + SC_SCALED) =
+                make_float4(ct * rk, ab.y, rk * __builtin_amdgcn_rcpf(ct), ct * rq);
+            *reinterpret_cast<float2*>(o + SC_KQ) = make_float2(my_qk * rq * rk, ct);
+            *reinterpret_cast<float4*>(o + SC_PLAIN) = make_float4(ab.x, ab.y, rk, rq);
         }
     };
 

@@ -7,9 +7,12 @@ per second (GB/s) on the decode workload: 256 rows x 1 token, 32 v-heads /
 16 k-heads, 128x128 fp32 state per head, 8192 bf16 conv channels with 4
 taps, 1024-slot pool with pages padded to 4 KiB, 90 % of the rows warm.
 Alongside: varlen prefill tokens/s (8 sequences of U{512..4096} tokens, 16
-heads) and the cross-layer restore GB/s (48 GDN layers of a 64-layer stack,
-64 ops, a quarter of them misses).  Inputs are synthetic and resident in HBM
-before timing; timing uses HIP events on the stream the kernels run on.
+heads; also 64 x 1000 tokens at 32 heads) with its flop rate against the fp32
+vector peak, and the cross-layer restore GB/s (48 GDN layers of a 64-layer
+stack, 64 ops, a quarter of them misses).  Inputs are synthetic and resident
+in HBM before timing; timing uses HIP events on the stream the kernels run
+on: `value` comes from K decode steps between one pair of events, the
+per-launch percentiles and the secondary figures from one pair per call.
 The CPU baseline is the oracle timed on this host on the same decode batch.
 """
 from __future__ import annotations
@@ -26,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak (packed FMA)
 
 METRIC = "GDN decode state GB/s (% HBM peak) + prefill tokens/s, 32 heads x 128x128 fp32"
 
@@ -81,6 +85,28 @@ def measured_traffic(profile: str, sources) -> "int | None":
     return nbytes if digest == h.hexdigest() else None
 
 
+def prefill_flops(inp) -> int:
+    """Algorithmic flops: per token, 6 dk dv per v-head (decay, S k, rank-1
+    update, S q as multiply-adds) and 2 W per conv channel."""
+    g = inp.geom
+    return inp.total_tokens * (g.Hv * 6 * g.dk * g.dv + 2 * g.W * g.C)
+
+
+def per_call(fn, n, stream):
+    """Each of n calls bracketed by its own pair of events: p10 / p50 / p90 in ms."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.sort([a.elapsed_time(b) for a, b in ev])
+    return {"p10": float(np.percentile(t, 10)), "p50": float(np.percentile(t, 50)),
+            "p90": float(np.percentile(t, 90))}
+
+
 def timed(fn, steps, warmup, stream):
     import torch
     for _ in range(warmup):
@@ -118,9 +144,9 @@ def bench_decode(steps, warmup):
     args = gdn.make_step_args(dev(inp.x), dev(inp.conv_w), None, dev(inp.alpha), dev(inp.beta),
                               dev(inp.state_indices), dev(inp.has_initial_state), out, 1.0, 1e-6)
     stream = torch.cuda.current_stream()
-    ms = timed(lambda: gdn.gdn_decode_step(h, 0, inp.num_seqs, args, stream), steps, warmup,
-               stream)
-    return inp, ms, decode_bytes(inp)
+    step = lambda: gdn.gdn_decode_step(h, 0, inp.num_seqs, args, stream)  # noqa: E731
+    ms = timed(step, steps, warmup, stream)
+    return inp, ms, decode_bytes(inp), per_call(step, steps, stream)
 
 
 def bench_prefill(steps, warmup):
@@ -138,9 +164,10 @@ def bench_prefill(steps, warmup):
                               dev(inp.state_indices), dev(inp.has_initial_state), out, 1.0, 1e-6)
     cu = dev(inp.cu_seqlens)
     stream = torch.cuda.current_stream()
-    ms = timed(lambda: gdn.gdn_prefill_varlen(h, 0, inp.num_seqs, cu, inp.max_seqlen,
-                                              inp.total_tokens, args, stream),
-               max(2, steps), max(1, warmup), stream)
+    call = lambda: gdn.gdn_prefill_varlen(h, 0, inp.num_seqs, cu, inp.max_seqlen,  # noqa: E731
+                                          inp.total_tokens, args, stream)
+    timed(call, 1, max(1, warmup), stream)
+    pc = per_call(call, max(2, steps), stream)
     # the same call emitting every sequence's state at its last 256-token block
     # boundary into a spare slot
     lens = np.diff(inp.cu_seqlens)
@@ -148,11 +175,44 @@ def bench_prefill(steps, warmup):
     ck_slot = dev(np.array([s for s in range(g.num_slots) if s not in used][:inp.num_seqs],
                            np.int32))
     ck_len = dev((lens // 256 * 256).astype(np.int32))
-    ms_ck = timed(lambda: gdn.gdn_prefill_varlen_checkpoint(h, 0, inp.num_seqs, cu,
+    ck = per_call(lambda: gdn.gdn_prefill_varlen_checkpoint(h, 0, inp.num_seqs, cu,
                                                             inp.max_seqlen, inp.total_tokens,
                                                             args, ck_slot, ck_len, stream),
-                  max(2, steps), max(1, warmup), stream)
-    return inp, ms, ms_ck
+                  max(2, steps), stream)
+    return inp, pc, ck["p50"]
+
+
+def bench_prefill_32heads(steps, warmup, n_seq=64, seq_len=1000):
+    """Prefill at the decode geometry (32 v-heads / 16 k-heads, 8192 channels):
+    64 sequences of 1000 tokens from a cold start, inputs drawn on the device."""
+    import torch
+    import hybrid_linear_attention_slot_amd as gdn
+    import workloads as wl
+
+    g = wl.decode_geometry(num_slots=n_seq)
+    pool = torch.zeros((g.num_slots, g.page_stride), dtype=torch.uint8, device="cuda")
+    h = gdn.gdn_pool_create([pool], g.num_slots, g.page_stride, g.conv_off, g.ssm_off, g.C,
+                            g.W, g.Hk, g.Hv, g.dk, g.dv)
+    gen = wl.device_generator(32, n_seq, seq_len)
+    T = n_seq * seq_len
+    x = wl.device_x(gen, T, g.C)
+    alpha, beta = wl.device_gates(gen, T, g.Hv)
+    rng = wl.rng_for(32)
+    w, _ = wl.draw_conv_params(rng, g.C, g.W, bias=False)
+    out = torch.empty((T, g.Hv, g.dv), dtype=torch.int16, device="cuda")
+    idx = torch.arange(n_seq, dtype=torch.int32, device="cuda")
+    hs = torch.zeros(n_seq, dtype=torch.uint8, device="cuda")
+    args = gdn.make_step_args(x, dev(w), None, alpha, beta, idx, hs, out, 1.0, 1e-6)
+    cu = torch.arange(0, T + 1, seq_len, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: gdn.gdn_prefill_varlen(h, 0, n_seq, cu, seq_len, T, args, stream)  # noqa: E731
+    timed(call, 1, max(1, warmup // 2), stream)
+    pc = per_call(call, max(2, steps // 5), stream)
+    del pool, x, out
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": round(T / (pc["p50"] * 1e-3), 1), "ms_per_call": round(pc["p50"], 4),
+            "workload": f"{n_seq} seqs x {seq_len} tokens, 32 v-heads/16 k-heads, 128x128 fp32, "
+                        "cold start (the continuation run's shape)"}
 
 
 def bench_restore(steps, warmup):
@@ -168,8 +228,9 @@ def bench_restore(steps, warmup):
     hs = torch.ones(len(ops), dtype=torch.uint8, device="cuda")
     op_list = ops.tolist()
     stream = torch.cuda.current_stream()
-    ms = timed(lambda: gdn.gdn_restore_slots(h, op_list, hs, stream), max(2, steps),
-               max(1, warmup), stream)
+    call = lambda: gdn.gdn_restore_slots(h, op_list, hs, stream)  # noqa: E731
+    timed(call, 1, max(1, warmup), stream)
+    ms = per_call(call, max(2, steps), stream)["p50"]
     hits = int((ops[:, 1] >= 0).sum())
     nbytes = 2 * hits * int(linear.sum()) * (g.ssm_region_bytes + g.conv_region_bytes)
     snap = bench_snapshot(h, int(ops[0, 0]), int(ops[1, 0]),
@@ -293,25 +354,34 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
-    inp, ms, nbytes = bench_decode(a.steps, a.warmup)
+    inp, ms, nbytes, dpc = bench_decode(a.steps, a.warmup)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    pinp, pms, pms_ck = bench_prefill(a.steps, a.warmup)
+    pinp, ppc, pms_ck = bench_prefill(a.steps, a.warmup)
+    pms = ppc["p50"]
+    pflops = prefill_flops(pinp) / (pms * 1e-3) / 1e12
     prefill = {"tokens_per_s": round(pinp.total_tokens / (pms * 1e-3), 1),
-               "ms_per_call": round(pms, 4), "tokens": pinp.total_tokens,
+               "ms_per_call": round(pms, 4),
+               "ms_p10_p90": [round(ppc["p10"], 4), round(ppc["p90"], 4)],
+               "tokens": pinp.total_tokens,
                "max_seqlen": pinp.max_seqlen,
                "us_per_token_critical_path": round(pms * 1e3 / pinp.max_seqlen, 4),
                "gb_per_s": round(prefill_bytes(pinp) / (pms * 1e-3) / 1e9, 2),
+               "tflops": round(pflops, 2),
+               "frac_of_fp32_vector_peak": round(pflops / FP32_VECTOR_PEAK_TFLOPS, 4),
                "workload": "8 seqs, lengths U{512..4096}, 16 v-heads/8 k-heads, 128x128 fp32, "
                            "4 warm + 4 cold",
                "ms_per_call_with_checkpoints": round(pms_ck, 4),
                "checkpoints": "each sequence's state at its last 256-token boundary emitted "
-                              "into a spare slot (gdn_prefill_varlen_checkpoint)"}
+                              "into a spare slot (gdn_prefill_varlen_checkpoint)",
+               "timing": "median of per-call HIP event pairs"}
+    prefill["heads_32"] = bench_prefill_32heads(a.steps, a.warmup)
     restore = None
     if not a.no_restore:
         rms, rbytes, hits, nlin, snap = bench_restore(a.steps, a.warmup)
         restore = {"gb_per_s": round(rbytes / (rms * 1e-3) / 1e9, 2), "ms_per_call": round(rms, 4),
                    "bytes": rbytes, "hits": hits, "gdn_layers": nlin,
                    "frac_of_hbm_peak": round(rbytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "timing": "median of per-call HIP event pairs",
                    "snapshot_one_slot": snap}
     line = {
         "metric": METRIC,
@@ -321,6 +391,7 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms, 5),
+        "per_launch_us": {k: round(v * 1e3, 2) for k, v in dpc.items()},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -49,8 +49,8 @@ bool prefill_supported(int dk, int dv, int W);
 int launch_decode(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn_step_args* a,
                   hipStream_t stream);
 // ckpt_slot / ckpt_len: NULL, or device int32 [num_seqs] (checkpoint emission)
-int launch_prefill(const gdn_pool* pool, int32_t layer, int32_t num_seqs, const int32_t* cu,
-                   const gdn_step_args* a, const int32_t* ckpt_slot, const int32_t* ckpt_len,
-                   hipStream_t stream);
+int launch_prefill(const gdn_pool* pool, int32_t layer, int32_t num_seqs, int64_t total_tokens,
+                   const int32_t* cu, const gdn_step_args* a, const int32_t* ckpt_slot,
+                   const int32_t* ckpt_len, hipStream_t stream);
 
 } // namespace gdn

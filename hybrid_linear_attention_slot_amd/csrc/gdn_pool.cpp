@@ -126,14 +126,9 @@ int gdn_pool_create(const gdn_pool_desc* d, gdn_pool** out)
                     (long long)d->page_stride_bytes);
     if (overlaps(d->conv_offset_bytes, conv, d->ssm_offset_bytes, ssm))
         return fail(GDN_EOVERLAP, "window and state regions overlap");
-    int32_t n_linear = 0;
-    for (int32_t l = 0; l < d->num_layers; ++l) {
-        if (d->layer_base[l] == nullptr)
-            continue;
-        if (!aligned16(d->layer_base[l]))
+    for (int32_t l = 0; l < d->num_layers; ++l)
+        if (d->layer_base[l] != nullptr && !aligned16(d->layer_base[l]))
             return fail(GDN_EALIGN, "layer_base[%d] is not 16-byte aligned", l);
-        ++n_linear;
-    }
     gdn_pool* p = new (std::nothrow) gdn_pool();
     if (!p)
         return fail(GDN_EINVAL, "out of host memory");
@@ -145,7 +140,6 @@ int gdn_pool_create(const gdn_pool_desc* d, gdn_pool** out)
             p->linear.push_back(l);
     p->ssm_bytes = ssm;
     p->conv_bytes = conv;
-    (void)n_linear;
     *out = p;
     return GDN_OK;
 }
@@ -309,7 +303,7 @@ int gdn_decode_step(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn
                     d.head_v_dim, d.conv_width);
     if (rows == 0)
         return GDN_OK;
-    if (!aligned16(a->out) && ((reinterpret_cast<uintptr_t>(a->out) & 7u) != 0))
+    if ((reinterpret_cast<uintptr_t>(a->out) & 7u) != 0)
         return fail(GDN_EALIGN, "out must be 8-byte aligned");
     if ((reinterpret_cast<uintptr_t>(a->x) & 3u) != 0 ||
         (reinterpret_cast<uintptr_t>(a->conv_w) & 3u) != 0 ||
@@ -344,8 +338,8 @@ int prefill_common(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
     if ((reinterpret_cast<uintptr_t>(a->conv_w) & 3u) != 0 ||
         (reinterpret_cast<uintptr_t>(a->conv_b) & 3u) != 0)
         return fail(GDN_EALIGN, "conv_w and conv_b must be 4-byte aligned");
-    return gdn::launch_prefill(pool, layer, num_seqs, cu_seqlens, a, ckpt_slot, ckpt_len,
-                               reinterpret_cast<hipStream_t>(stream));
+    return gdn::launch_prefill(pool, layer, num_seqs, total_tokens, cu_seqlens, a, ckpt_slot,
+                               ckpt_len, reinterpret_cast<hipStream_t>(stream));
 }
 } // namespace
 

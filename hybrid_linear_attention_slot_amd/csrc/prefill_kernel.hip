@@ -79,6 +79,7 @@ struct PrefillParams {
     int64_t conv_off;
     int32_t num_slots;
     int32_t num_seqs;
+    int64_t total_tokens; // rows of x / alpha / beta / out
     int32_t C;
     int32_t Hk;
     int32_t Hv;
@@ -187,10 +188,12 @@ void prefill_kernel(PrefillParams p)
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform: role and token
     const int lane = tid & 63;                                 // indices go to scalar registers
-    const int tb = p.cu[n];
-    const int L = p.cu[n + 1] - tb;
-    if (L <= 0)
+    // a sequence whose range is empty or not inside [0, total_tokens) is skipped
+    const int64_t tb64 = p.cu[n], te64 = p.cu[n + 1];
+    if (tb64 < 0 || te64 <= tb64 || te64 > p.total_tokens)
         return;
+    const int tb = int(tb64);
+    const int L = int(te64 - tb64);
     const int64_t out_tok = int64_t(p.Hv) * DV; // out elements per token
     uint16_t* out_base = p.out + int64_t(tb) * out_tok + int64_t(h) * DV + sl * ISZ;
     const int slot = p.state_indices[n];
@@ -634,6 +637,7 @@ struct WindowParams {
     int32_t num_slots;
     int32_t C;
     int32_t W;
+    int64_t total_tokens;
     const int32_t* cu;
     const uint16_t* x;
     const int32_t* state_indices;
@@ -651,10 +655,13 @@ __global__ __launch_bounds__(kWinThreads) void prefill_window_kernel(WindowParam
     const int c = (blockIdx.x - n * cblocks) * kWinThreads + threadIdx.x;
     if (c >= p.C)
         return;
-    const int tb = p.cu[n];
-    const int L = p.cu[n + 1] - tb;
+    const int64_t tb64 = p.cu[n], te64 = p.cu[n + 1];
+    if (tb64 < 0 || te64 <= tb64 || te64 > p.total_tokens) // as in prefill_kernel
+        return;
+    const int tb = int(tb64);
+    const int L = int(te64 - tb64);
     const int slot = p.state_indices[n];
-    if (L <= 0 || slot < 0 || slot >= p.num_slots)
+    if (slot < 0 || slot >= p.num_slots)
         return;
     const bool warm = p.hs[n] != 0;
     uint16_t* win = reinterpret_cast<uint16_t*>(p.layer + int64_t(slot) * p.page_stride +
@@ -691,9 +698,9 @@ __global__ __launch_bounds__(kWinThreads) void prefill_window_kernel(WindowParam
 }
 
 template <int DK, int DV, int W>
-int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, const int32_t* cu,
-                     const gdn_step_args* a, const int32_t* ckpt_slot, const int32_t* ckpt_len,
-                     hipStream_t stream)
+int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, int64_t total_tokens,
+                     const int32_t* cu, const gdn_step_args* a, const int32_t* ckpt_slot,
+                     const int32_t* ckpt_len, hipStream_t stream)
 {
     using Sh = PrefillShape<DK, DV>;
     const gdn_pool_desc& d = pool->desc;
@@ -704,6 +711,7 @@ int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, cons
     p.conv_off = d.conv_offset_bytes;
     p.num_slots = int32_t(d.num_slots);
     p.num_seqs = num_seqs;
+    p.total_tokens = total_tokens;
     p.C = d.conv_channels;
     p.Hk = d.num_k_heads;
     p.Hv = d.num_v_heads;
@@ -735,6 +743,7 @@ int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, cons
     w.num_slots = p.num_slots;
     w.C = p.C;
     w.W = W;
+    w.total_tokens = total_tokens;
     w.cu = cu;
     w.x = a->x;
     w.state_indices = a->state_indices;
@@ -751,13 +760,13 @@ int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, cons
 }
 
 template <int DK>
-int dispatch_w(const gdn_pool* pool, int32_t layer, int32_t num_seqs, const int32_t* cu,
+int dispatch_w(const gdn_pool* pool, int32_t layer, int32_t num_seqs, int64_t T, const int32_t* cu,
                const gdn_step_args* a, const int32_t* cs, const int32_t* cl, hipStream_t stream)
 {
     switch (pool->desc.conv_width) {
-    case 2: return launch_prefill_t<DK, DK, 2>(pool, layer, num_seqs, cu, a, cs, cl, stream);
-    case 3: return launch_prefill_t<DK, DK, 3>(pool, layer, num_seqs, cu, a, cs, cl, stream);
-    case 4: return launch_prefill_t<DK, DK, 4>(pool, layer, num_seqs, cu, a, cs, cl, stream);
+    case 2: return launch_prefill_t<DK, DK, 2>(pool, layer, num_seqs, T, cu, a, cs, cl, stream);
+    case 3: return launch_prefill_t<DK, DK, 3>(pool, layer, num_seqs, T, cu, a, cs, cl, stream);
+    case 4: return launch_prefill_t<DK, DK, 4>(pool, layer, num_seqs, T, cu, a, cs, cl, stream);
     default: return fail(GDN_EUNSUPPORTED, "prefill: conv width %d", pool->desc.conv_width);
     }
 }
@@ -769,16 +778,16 @@ bool prefill_supported(int dk, int dv, int W)
     return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128) && W >= 2 && W <= 4;
 }
 
-int launch_prefill(const gdn_pool* pool, int32_t layer, int32_t num_seqs, const int32_t* cu,
-                   const gdn_step_args* a, const int32_t* ckpt_slot, const int32_t* ckpt_len,
-                   hipStream_t stream)
+int launch_prefill(const gdn_pool* pool, int32_t layer, int32_t num_seqs, int64_t total_tokens,
+                   const int32_t* cu, const gdn_step_args* a, const int32_t* ckpt_slot,
+                   const int32_t* ckpt_len, hipStream_t stream)
 {
     const int32_t *cs = ckpt_slot, *cl = ckpt_len;
     switch (pool->desc.head_k_dim) {
-    case 16: return dispatch_w<16>(pool, layer, num_seqs, cu, a, cs, cl, stream);
-    case 32: return dispatch_w<32>(pool, layer, num_seqs, cu, a, cs, cl, stream);
-    case 64: return dispatch_w<64>(pool, layer, num_seqs, cu, a, cs, cl, stream);
-    case 128: return dispatch_w<128>(pool, layer, num_seqs, cu, a, cs, cl, stream);
+    case 16: return dispatch_w<16>(pool, layer, num_seqs, total_tokens, cu, a, cs, cl, stream);
+    case 32: return dispatch_w<32>(pool, layer, num_seqs, total_tokens, cu, a, cs, cl, stream);
+    case 64: return dispatch_w<64>(pool, layer, num_seqs, total_tokens, cu, a, cs, cl, stream);
+    case 128: return dispatch_w<128>(pool, layer, num_seqs, total_tokens, cu, a, cs, cl, stream);
     default: return fail(GDN_EUNSUPPORTED, "prefill: head dim %d", pool->desc.head_k_dim);
     }
 }

@@ -187,9 +187,11 @@ int gdn_decode_step(const gdn_pool* pool, int32_t layer, int32_t rows,
  * beta / out and owns slot state_indices[n].  The state is carried on chip
  * from token to token; the final window and state are written back in place.
  * cu_seqlens_dev: device int32 [num_seqs + 1], non-decreasing, cu[0] == 0,
- * cu[num_seqs] == total_tokens (not checkable on the host).  max_seqlen is an
- * upper bound of the lengths (host hint).  A zero-length sequence leaves its
- * slot untouched.  Alignment: x and out 16-byte aligned (the inputs are read
+ * cu[num_seqs] == total_tokens (not checkable on the host without a
+ * synchronisation; the kernels skip a sequence whose range is empty or not
+ * inside [0, total_tokens): no memory access, its slot and output rows are
+ * left as they were).  max_seqlen is an upper bound of the lengths (host
+ * hint).  A zero-length sequence leaves its slot untouched.  Alignment: x and out 16-byte aligned (the inputs are read
  * and the outputs written in 16-byte pieces), conv_w and conv_b 4-byte
  * aligned.  Errors as for gdn_decode_step. */
 int gdn_prefill_varlen(const gdn_pool* pool, int32_t layer, int32_t num_seqs,

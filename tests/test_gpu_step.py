@@ -131,6 +131,30 @@ def test_prefill_extreme_decays_match_oracle(d):
     assert np.array_equal(a.host(), b.host()), "split run's pages differ"
 
 
+def test_prefill_skips_sequences_outside_total_tokens():
+    """cu_seqlens is not checkable on the host: a sequence whose range is empty
+    or runs past total_tokens is skipped (its slot and output rows untouched);
+    the well-formed ones are computed as usual."""
+    g = wl.make_geometry(8, Hk=1, Hv=2, dk=32, dv=32, W=4, page_align=128, extra_pad=128)
+    inp, img = case(g, 950, [20, 12, 8], [1, 1, 0], bias=True)
+    bad = dataclasses.replace(inp, cu_seqlens=np.array([0, 20, 48, 40], np.int32))
+    dp = DevicePool(g, [img])
+    log("prefill with cu = [0, 20, 48, 40], total_tokens = 40")
+    t = run_prefill(dp, 0, bad)
+    torch.cuda.synchronize()
+    got = dp.host()
+    out = u16(t["out"])
+    assert (out[20:] == 0x7FC0).all(), "skipped sequences' output rows were written"
+    ref = img.copy()
+    first = dataclasses.replace(inp, x=inp.x[:20], alpha=inp.alpha[:20], beta=inp.beta[:20],
+                                cu_seqlens=np.array([0, 20], np.int32),
+                                state_indices=inp.state_indices[:1],
+                                has_initial_state=inp.has_initial_state[:1])
+    o64, _ = oracle_layer(ref, first)
+    check_outputs(out[:20], o64, "well-formed sequence")
+    check_pages(g, got, ref, slots=inp.state_indices[:1], what="skipped sequences")
+
+
 def test_prefill_many_short_sequences():
     """More sequences than one wave can rank (the placement by length then
     keeps the natural order), lengths 0..20 including many shorter than the

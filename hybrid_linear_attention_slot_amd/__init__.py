@@ -27,11 +27,12 @@ GDN_ENOSLOT = -7
 GDN_ESTATE = -8
 GDN_EIO = -9
 GDN_ECORRUPT = -10
+GDN_ENOMEM = -11
 
 ERROR_NAMES = {GDN_EINVAL: "GDN_EINVAL", GDN_ERANGE: "GDN_ERANGE", GDN_EOVERLAP: "GDN_EOVERLAP",
                GDN_EALIGN: "GDN_EALIGN", GDN_EUNSUPPORTED: "GDN_EUNSUPPORTED",
                GDN_EHIP: "GDN_EHIP", GDN_ENOSLOT: "GDN_ENOSLOT", GDN_ESTATE: "GDN_ESTATE",
-               GDN_EIO: "GDN_EIO", GDN_ECORRUPT: "GDN_ECORRUPT"}
+               GDN_EIO: "GDN_EIO", GDN_ECORRUPT: "GDN_ECORRUPT", GDN_ENOMEM: "GDN_ENOMEM"}
 
 GDN_SLOT_FREE, GDN_SLOT_LIVE, GDN_SLOT_CHECKPOINT, GDN_SLOT_RESERVED = 0, 1, 2, 3
 

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <new>
 #include <vector>
 
 #include "gdn.h"
@@ -20,9 +21,26 @@ struct gdn_pool {
 namespace gdn {
 
 // Record `code` with a printf-style message for gdn_last_error(); returns code.
+// Allocates nothing (a fixed per-thread buffer), so it is safe under memory
+// exhaustion.
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 int check_launch(const char* what); // GDN_OK, or GDN_EHIP after a launch error
+
+// Runs f(), which returns a GDN code; a host allocation failure becomes
+// GDN_ENOMEM and any other C++ exception GDN_EINVAL, so that none crosses the
+// C ABI.
+template <class F>
+int guarded(F&& f) noexcept
+{
+    try {
+        return f();
+    } catch (const std::bad_alloc&) {
+        return fail(GDN_ENOMEM, "out of host memory");
+    } catch (...) {
+        return fail(GDN_EINVAL, "internal error");
+    }
+}
 
 // ---- restore / gather / scatter (copy_kernels.hip) ----------------------
 struct HitPair {

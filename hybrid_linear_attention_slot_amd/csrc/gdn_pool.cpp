@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <memory>
 #include <new>
 #include <string>
 #include <unordered_set>
@@ -14,21 +15,19 @@
 namespace gdn {
 
 namespace {
-thread_local std::string g_last_error;
+thread_local char g_last_error[512];
 }
 
 int fail(int code, const char* fmt, ...)
 {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
     va_end(ap);
-    g_last_error = buf;
     return code;
 }
 
-void clear_error() { g_last_error.clear(); }
+void clear_error() { g_last_error[0] = '\0'; }
 
 int check_launch(const char* what)
 {
@@ -81,11 +80,91 @@ int check_step_args(const gdn_pool* pool, int32_t layer, const gdn_step_args* a)
     return GDN_OK;
 }
 
+int describe(const gdn_pool* pool, char* buf, size_t len)
+{
+    const gdn_pool_desc& d = pool->desc;
+    std::string s;
+    char line[512];
+    const int64_t payload_end =
+        std::max(d.conv_offset_bytes + pool->conv_bytes, d.ssm_offset_bytes + pool->ssm_bytes);
+    snprintf(line, sizeof line,
+             "[gdn-pool] layers=%d (linear=%zu, attention-only=%zu) slots=%lld "
+             "page_stride=%lldB padding_after_payload=%lldB\n",
+             d.num_layers, pool->linear.size(), d.num_layers - pool->linear.size(),
+             (long long)d.num_slots, (long long)d.page_stride_bytes,
+             (long long)(d.page_stride_bytes - payload_end));
+    s += line;
+    snprintf(line, sizeof line,
+             "[gdn-pool] ssm: fp32 [Hv=%d][dk=%d][dv=%d] = %lldB at offset %lld, "
+             "slot stride %lld elements\n",
+             d.num_v_heads, d.head_k_dim, d.head_v_dim, (long long)pool->ssm_bytes,
+             (long long)d.ssm_offset_bytes, (long long)(d.page_stride_bytes / 4));
+    s += line;
+    snprintf(line, sizeof line,
+             "[gdn-pool] conv: bf16 [W-1=%d][C=%d] = %lldB at offset %lld, "
+             "slot stride %lld elements (Hk=%d)\n",
+             d.conv_width - 1, d.conv_channels, (long long)pool->conv_bytes,
+             (long long)d.conv_offset_bytes, (long long)(d.page_stride_bytes / 2),
+             d.num_k_heads);
+    s += line;
+    s += "[gdn-pool] attention-only layers:";
+    for (int32_t l = 0; l < d.num_layers; ++l)
+        if (!pool->bases[l]) {
+            snprintf(line, sizeof line, " %d", l);
+            s += line;
+        }
+    s += "\n";
+    if (buf && len > 0) {
+        size_t n = std::min(len - 1, s.size());
+        memcpy(buf, s.data(), n);
+        buf[n] = '\0';
+    }
+    return (int)s.size();
+}
+
+int restore(const gdn_pool* pool, const gdn_restore_op* ops, int32_t n_ops, uint8_t* hs_dev,
+            gdn_stream_t stream)
+{
+    const int64_t ns = pool->desc.num_slots;
+    std::vector<gdn::HitPair> pairs;
+    std::vector<gdn::HsWrite> hs;
+    std::unordered_set<int32_t> dsts;
+    for (int32_t i = 0; i < n_ops; ++i) {
+        const gdn_restore_op& op = ops[i];
+        if (!op.requested)
+            continue;
+        if (op.src_slot < 0) {
+            hs.push_back({i, 0});
+            continue;
+        }
+        if (op.src_slot >= ns || op.dst_slot < 0 || op.dst_slot >= ns)
+            return fail(GDN_ERANGE, "op %d: dst %d / src %d outside [0, %lld)", i, op.dst_slot,
+                        op.src_slot, (long long)ns);
+        if (!dsts.insert(op.dst_slot).second)
+            return fail(GDN_EOVERLAP, "op %d: dst slot %d is named twice", i, op.dst_slot);
+        pairs.push_back({op.dst_slot, op.src_slot});
+        hs.push_back({i, pool->linear.empty() ? 0 : 1});
+    }
+    for (const gdn::HitPair& p : pairs)
+        if (dsts.count(p.src))
+            return fail(GDN_EOVERLAP, "src slot %d is also a dst slot", p.src);
+    const bool soft_failure = !pairs.empty() && pool->linear.empty();
+    if (pool->linear.empty())
+        pairs.clear();
+    int rc = gdn::launch_restore(pool, pairs, hs, hs_dev, reinterpret_cast<hipStream_t>(stream));
+    if (rc != GDN_OK)
+        return rc;
+    if (soft_failure)
+        return fail(GDN_WARN_COLD_FALLBACK,
+                    "no layer has a state pool: restored rows fall back to a cold start");
+    return GDN_OK;
+}
+
 } // namespace
 
 extern "C" {
 
-const char* gdn_last_error(void) { return gdn::g_last_error.c_str(); }
+const char* gdn_last_error(void) { return gdn::g_last_error; }
 
 int gdn_pool_create(const gdn_pool_desc* d, gdn_pool** out)
 {
@@ -129,19 +208,19 @@ int gdn_pool_create(const gdn_pool_desc* d, gdn_pool** out)
     for (int32_t l = 0; l < d->num_layers; ++l)
         if (d->layer_base[l] != nullptr && !aligned16(d->layer_base[l]))
             return fail(GDN_EALIGN, "layer_base[%d] is not 16-byte aligned", l);
-    gdn_pool* p = new (std::nothrow) gdn_pool();
-    if (!p)
-        return fail(GDN_EINVAL, "out of host memory");
-    p->desc = *d;
-    p->bases.assign(d->layer_base, d->layer_base + d->num_layers);
-    p->desc.layer_base = p->bases.data();
-    for (int32_t l = 0; l < d->num_layers; ++l)
-        if (p->bases[l])
-            p->linear.push_back(l);
-    p->ssm_bytes = ssm;
-    p->conv_bytes = conv;
-    *out = p;
-    return GDN_OK;
+    return gdn::guarded([&] {
+        std::unique_ptr<gdn_pool> p(new gdn_pool());
+        p->desc = *d;
+        p->bases.assign(d->layer_base, d->layer_base + d->num_layers);
+        p->desc.layer_base = p->bases.data();
+        for (int32_t l = 0; l < d->num_layers; ++l)
+            if (p->bases[l])
+                p->linear.push_back(l);
+        p->ssm_bytes = ssm;
+        p->conv_bytes = conv;
+        *out = p.release();
+        return int(GDN_OK);
+    });
 }
 
 void gdn_pool_destroy(gdn_pool* pool) { delete pool; }
@@ -161,44 +240,7 @@ int gdn_pool_describe(const gdn_pool* pool, char* buf, size_t len)
 {
     if (!pool)
         return fail(GDN_EINVAL, "pool is NULL");
-    const gdn_pool_desc& d = pool->desc;
-    std::string s;
-    char line[512];
-    const int64_t payload_end =
-        std::max(d.conv_offset_bytes + pool->conv_bytes, d.ssm_offset_bytes + pool->ssm_bytes);
-    snprintf(line, sizeof line,
-             "[gdn-pool] layers=%d (linear=%zu, attention-only=%zu) slots=%lld "
-             "page_stride=%lldB padding_after_payload=%lldB\n",
-             d.num_layers, pool->linear.size(), d.num_layers - pool->linear.size(),
-             (long long)d.num_slots, (long long)d.page_stride_bytes,
-             (long long)(d.page_stride_bytes - payload_end));
-    s += line;
-    snprintf(line, sizeof line,
-             "[gdn-pool] ssm: fp32 [Hv=%d][dk=%d][dv=%d] = %lldB at offset %lld, "
-             "slot stride %lld elements\n",
-             d.num_v_heads, d.head_k_dim, d.head_v_dim, (long long)pool->ssm_bytes,
-             (long long)d.ssm_offset_bytes, (long long)(d.page_stride_bytes / 4));
-    s += line;
-    snprintf(line, sizeof line,
-             "[gdn-pool] conv: bf16 [W-1=%d][C=%d] = %lldB at offset %lld, "
-             "slot stride %lld elements (Hk=%d)\n",
-             d.conv_width - 1, d.conv_channels, (long long)pool->conv_bytes,
-             (long long)d.conv_offset_bytes, (long long)(d.page_stride_bytes / 2),
-             d.num_k_heads);
-    s += line;
-    s += "[gdn-pool] attention-only layers:";
-    for (int32_t l = 0; l < d.num_layers; ++l)
-        if (!pool->bases[l]) {
-            snprintf(line, sizeof line, " %d", l);
-            s += line;
-        }
-    s += "\n";
-    if (buf && len > 0) {
-        size_t n = std::min(len - 1, s.size());
-        memcpy(buf, s.data(), n);
-        buf[n] = '\0';
-    }
-    return (int)s.size();
+    return gdn::guarded([&] { return describe(pool, buf, len); });
 }
 
 int gdn_restore_slots(const gdn_pool* pool, const gdn_restore_op* ops, int32_t n_ops,
@@ -213,39 +255,7 @@ int gdn_restore_slots(const gdn_pool* pool, const gdn_restore_op* ops, int32_t n
         return GDN_OK;
     if (!ops || !hs_dev)
         return fail(GDN_EINVAL, "ops and has_initial_state must not be NULL");
-    const int64_t ns = pool->desc.num_slots;
-    std::vector<gdn::HitPair> pairs;
-    std::vector<gdn::HsWrite> hs;
-    std::unordered_set<int32_t> dsts;
-    for (int32_t i = 0; i < n_ops; ++i) {
-        const gdn_restore_op& op = ops[i];
-        if (!op.requested)
-            continue;
-        if (op.src_slot < 0) {
-            hs.push_back({i, 0});
-            continue;
-        }
-        if (op.src_slot >= ns || op.dst_slot < 0 || op.dst_slot >= ns)
-            return fail(GDN_ERANGE, "op %d: dst %d / src %d outside [0, %lld)", i, op.dst_slot,
-                        op.src_slot, (long long)ns);
-        if (!dsts.insert(op.dst_slot).second)
-            return fail(GDN_EOVERLAP, "op %d: dst slot %d is named twice", i, op.dst_slot);
-        pairs.push_back({op.dst_slot, op.src_slot});
-        hs.push_back({i, pool->linear.empty() ? 0 : 1});
-    }
-    for (const gdn::HitPair& p : pairs)
-        if (dsts.count(p.src))
-            return fail(GDN_EOVERLAP, "src slot %d is also a dst slot", p.src);
-    const bool soft_failure = !pairs.empty() && pool->linear.empty();
-    if (pool->linear.empty())
-        pairs.clear();
-    int rc = gdn::launch_restore(pool, pairs, hs, hs_dev, reinterpret_cast<hipStream_t>(stream));
-    if (rc != GDN_OK)
-        return rc;
-    if (soft_failure)
-        return fail(GDN_WARN_COLD_FALLBACK,
-                    "no layer has a state pool: restored rows fall back to a cold start");
-    return GDN_OK;
+    return gdn::guarded([&] { return restore(pool, ops, n_ops, hs_dev, stream); });
 }
 
 int gdn_gather_states(const gdn_pool* pool, int32_t layer, const int32_t* idx, int32_t n,

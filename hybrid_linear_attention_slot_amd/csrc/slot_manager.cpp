@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include <map>
+#include <memory>
 #include <set>
 #include <unordered_map>
 #include <unordered_set>
@@ -78,33 +79,24 @@ struct gdn_slot_manager {
             --slots[s].pins;
         pinned.clear();
     }
+    // undo a resolve (its reservations and pins); allocates nothing
+    void rollback()
+    {
+        for (const auto& p : promotions)
+            release(p.replacement);
+        drop_pins();
+        promotions.clear();
+        batch.clear();
+        pending = false;
+    }
 };
 
-extern "C" {
+namespace {
 
-int gdn_slots_create(int32_t num_slots, int32_t block_size, gdn_slot_manager** out)
+int add_sequence(gdn_slot_manager* m, int64_t seq_id, int32_t* live_slot)
 {
-    gdn::clear_error();
-    if (!out || num_slots < 1 || block_size < 1)
-        return fail(GDN_EINVAL, "slots: num_slots and block_size must be >= 1, out non-NULL");
-    auto* m = new gdn_slot_manager();
-    m->block = block_size;
-    m->slots.resize(size_t(num_slots));
-    for (int32_t s = 0; s < num_slots; ++s)
-        m->free_slots.insert(s);
-    *out = m;
-    return GDN_OK;
-}
-
-void gdn_slots_destroy(gdn_slot_manager* m) { delete m; }
-
-int gdn_slots_add_sequence(gdn_slot_manager* m, int64_t seq_id, int32_t* live_slot)
-{
-    gdn::clear_error();
-    if (!m || !live_slot)
-        return fail(GDN_EINVAL, "slots: NULL argument");
-    if (m->seqs.count(seq_id))
-        return fail(GDN_EINVAL, "slots: sequence %lld already has a live slot", (long long)seq_id);
+    // the map entry first: if it cannot be allocated, nothing has changed
+    gdn_slot_manager::Seq& q = m->seqs[seq_id];
     int32_t s = -1;
     if (!m->free_slots.empty()) {
         s = m->take_free();
@@ -116,42 +108,23 @@ int gdn_slots_add_sequence(gdn_slot_manager* m, int64_t seq_id, int32_t* live_sl
                 break;
             }
         }
-        if (s < 0)
+        if (s < 0) {
+            m->seqs.erase(seq_id);
             return fail(GDN_ENOSLOT, "slots: no free slot and no reclaimable checkpoint");
+        }
         m->table.erase(m->slots[s].hash);
         m->lru.erase(m->slots[s].stamp);
     }
     m->slots[s] = gdn_slot_manager::Slot{};
     m->slots[s].kind = GDN_SLOT_LIVE;
     m->slots[s].owner = seq_id;
-    m->seqs[seq_id] = gdn_slot_manager::Seq{s, false};
+    q = gdn_slot_manager::Seq{s, false};
     *live_slot = s;
     return GDN_OK;
 }
 
-int gdn_slots_remove_sequence(gdn_slot_manager* m, int64_t seq_id)
+int resolve(gdn_slot_manager* m, const gdn_slot_request* rows, int32_t n, gdn_linear_state_op* ops)
 {
-    gdn::clear_error();
-    if (!m)
-        return fail(GDN_EINVAL, "slots: NULL manager");
-    if (m->pending)
-        return fail(GDN_ESTATE, "slots: a resolved batch is pending");
-    auto it = m->seqs.find(seq_id);
-    if (it == m->seqs.end())
-        return fail(GDN_EINVAL, "slots: unknown sequence %lld", (long long)seq_id);
-    m->release(it->second.slot);
-    m->seqs.erase(it);
-    return GDN_OK;
-}
-
-int gdn_slots_resolve(gdn_slot_manager* m, const gdn_slot_request* rows, int32_t n,
-                      gdn_linear_state_op* ops)
-{
-    gdn::clear_error();
-    if (!m || n < 0 || (n > 0 && (!rows || !ops)))
-        return fail(GDN_EINVAL, "slots: bad resolve arguments");
-    if (m->pending)
-        return fail(GDN_ESTATE, "slots: the previous batch was neither committed nor aborted");
     std::unordered_set<int64_t> seen;
     for (int32_t i = 0; i < n; ++i) {
         if (!m->seqs.count(rows[i].seq_id))
@@ -213,13 +186,8 @@ int gdn_slots_resolve(gdn_slot_manager* m, const gdn_slot_request* rows, int32_t
     return GDN_OK;
 }
 
-int gdn_slots_commit(gdn_slot_manager* m)
+int commit(gdn_slot_manager* m)
 {
-    gdn::clear_error();
-    if (!m)
-        return fail(GDN_EINVAL, "slots: NULL manager");
-    if (!m->pending)
-        return fail(GDN_ESTATE, "slots: commit without a resolved batch");
     for (int64_t s : m->batch)
         m->seqs[s].initialized = true; // the forward wrote every row's live slot
     for (const auto& p : m->promotions) {
@@ -245,6 +213,83 @@ int gdn_slots_commit(gdn_slot_manager* m)
     return GDN_OK;
 }
 
+} // namespace
+
+extern "C" {
+
+int gdn_slots_create(int32_t num_slots, int32_t block_size, gdn_slot_manager** out)
+{
+    gdn::clear_error();
+    if (!out || num_slots < 1 || block_size < 1)
+        return fail(GDN_EINVAL, "slots: num_slots and block_size must be >= 1, out non-NULL");
+    return gdn::guarded([&] {
+        std::unique_ptr<gdn_slot_manager> m(new gdn_slot_manager());
+        m->block = block_size;
+        m->slots.resize(size_t(num_slots));
+        for (int32_t s = 0; s < num_slots; ++s)
+            m->free_slots.insert(s);
+        *out = m.release();
+        return int(GDN_OK);
+    });
+}
+
+void gdn_slots_destroy(gdn_slot_manager* m) { delete m; }
+
+int gdn_slots_add_sequence(gdn_slot_manager* m, int64_t seq_id, int32_t* live_slot)
+{
+    gdn::clear_error();
+    if (!m || !live_slot)
+        return fail(GDN_EINVAL, "slots: NULL argument");
+    if (m->seqs.count(seq_id))
+        return fail(GDN_EINVAL, "slots: sequence %lld already has a live slot", (long long)seq_id);
+    return gdn::guarded([&] { return add_sequence(m, seq_id, live_slot); });
+}
+
+int gdn_slots_remove_sequence(gdn_slot_manager* m, int64_t seq_id)
+{
+    gdn::clear_error();
+    if (!m)
+        return fail(GDN_EINVAL, "slots: NULL manager");
+    if (m->pending)
+        return fail(GDN_ESTATE, "slots: a resolved batch is pending");
+    auto it = m->seqs.find(seq_id);
+    if (it == m->seqs.end())
+        return fail(GDN_EINVAL, "slots: unknown sequence %lld", (long long)seq_id);
+    return gdn::guarded([&] {
+        m->release(it->second.slot); // the set insert may allocate
+        m->seqs.erase(it);
+        return int(GDN_OK);
+    });
+}
+
+int gdn_slots_resolve(gdn_slot_manager* m, const gdn_slot_request* rows, int32_t n,
+                      gdn_linear_state_op* ops)
+{
+    gdn::clear_error();
+    if (!m || n < 0 || (n > 0 && (!rows || !ops)))
+        return fail(GDN_EINVAL, "slots: bad resolve arguments");
+    if (m->pending)
+        return fail(GDN_ESTATE, "slots: the previous batch was neither committed nor aborted");
+    return gdn::guarded([&] {
+        try {
+            return resolve(m, rows, n, ops);
+        } catch (...) {
+            m->rollback();
+            throw;
+        }
+    });
+}
+
+int gdn_slots_commit(gdn_slot_manager* m)
+{
+    gdn::clear_error();
+    if (!m)
+        return fail(GDN_EINVAL, "slots: NULL manager");
+    if (!m->pending)
+        return fail(GDN_ESTATE, "slots: commit without a resolved batch");
+    return gdn::guarded([&] { return commit(m); });
+}
+
 int gdn_slots_abort(gdn_slot_manager* m)
 {
     gdn::clear_error();
@@ -252,13 +297,10 @@ int gdn_slots_abort(gdn_slot_manager* m)
         return fail(GDN_EINVAL, "slots: NULL manager");
     if (!m->pending)
         return fail(GDN_ESTATE, "slots: abort without a resolved batch");
-    for (const auto& p : m->promotions)
-        m->release(p.replacement);
-    m->drop_pins();
-    m->promotions.clear();
-    m->batch.clear();
-    m->pending = false;
-    return GDN_OK;
+    return gdn::guarded([&] {
+        m->rollback(); // the set inserts may allocate
+        return int(GDN_OK);
+    });
 }
 
 int gdn_slots_restore_ops(const gdn_linear_state_op* ops, int32_t n, gdn_restore_op* out)

@@ -129,39 +129,66 @@ void build_header(uint8_t* h, const Layout& L, uint64_t key, int64_t position,
     put<uint32_t>(h, kHeaderCrcAt, gdn_crc32c(0, h, kHeaderCrcAt));
 }
 
-// Reads and checks a whole file; GDN_OK, GDN_EIO or GDN_ECORRUPT.
-int read_checked(const char* path, std::vector<uint8_t>& buf)
+// An open snapshot file whose header has been read and checked.
+struct File {
+    int fd = -1;
+    uint8_t h[kHeader];
+    int64_t payload = 0; // bytes after the header, as the header states
+    ~File()
+    {
+        if (fd >= 0)
+            close(fd);
+    }
+};
+
+bool read_all(int fd, uint8_t* p, size_t n, off_t at)
 {
-    const int fd = open(path, O_RDONLY);
-    if (fd < 0)
+    while (n > 0) {
+        const ssize_t r = pread(fd, p, n, at);
+        if (r <= 0)
+            return false;
+        p += r;
+        n -= size_t(r);
+        at += r;
+    }
+    return true;
+}
+
+// Opens `path` and checks its identity, its header checksum and that its size
+// is the header's plus the payload the header states (nothing is allocated
+// before that); GDN_OK, GDN_EIO or GDN_ECORRUPT.
+int open_checked(const char* path, File& f)
+{
+    f.fd = open(path, O_RDONLY);
+    if (f.fd < 0)
         return fail(GDN_EIO, "snapshot: cannot open %s", path);
     struct stat st;
-    if (fstat(fd, &st) != 0) {
-        close(fd);
+    if (fstat(f.fd, &st) != 0)
         return fail(GDN_EIO, "snapshot: cannot stat %s", path);
-    }
-    buf.resize(size_t(st.st_size));
-    size_t got = 0;
-    while (got < buf.size()) {
-        const ssize_t r = read(fd, buf.data() + got, buf.size() - got);
-        if (r <= 0) {
-            close(fd);
-            return fail(GDN_EIO, "snapshot: read error on %s", path);
-        }
-        got += size_t(r);
-    }
-    close(fd);
-    const uint8_t* h = buf.data();
-    if (buf.size() < kHeader || memcmp(h, kMagic, 8) != 0 || get<uint32_t>(h, 8) != kVersion ||
+    if (uint64_t(st.st_size) < kHeader)
+        return fail(GDN_ECORRUPT, "snapshot: %s is shorter than a header", path);
+    if (!read_all(f.fd, f.h, kHeader, 0))
+        return fail(GDN_EIO, "snapshot: read error on %s", path);
+    const uint8_t* h = f.h;
+    if (memcmp(h, kMagic, 8) != 0 || get<uint32_t>(h, 8) != kVersion ||
         get<uint32_t>(h, 12) != kHeader)
         return fail(GDN_ECORRUPT, "snapshot: %s is not a version-%u state snapshot", path,
                     kVersion);
     if (get<uint32_t>(h, kHeaderCrcAt) != gdn_crc32c(0, h, kHeaderCrcAt))
         return fail(GDN_ECORRUPT, "snapshot: header checksum mismatch in %s", path);
-    const int64_t payload = get<int64_t>(h, 88);
-    if (payload < 0 || uint64_t(payload) != buf.size() - kHeader)
+    f.payload = get<int64_t>(h, 88);
+    if (f.payload < 0 || uint64_t(f.payload) != uint64_t(st.st_size) - kHeader)
         return fail(GDN_ECORRUPT, "snapshot: %s is truncated or has trailing bytes", path);
-    if (get<uint32_t>(h, 96) != gdn_crc32c(0, h + kHeader, size_t(payload)))
+    return GDN_OK;
+}
+
+// Reads the payload of a checked file and verifies its checksum.
+int read_payload(const char* path, const File& f, std::vector<uint8_t>& buf)
+{
+    buf.resize(size_t(f.payload));
+    if (!read_all(f.fd, buf.data(), buf.size(), off_t(kHeader)))
+        return fail(GDN_EIO, "snapshot: read error on %s", path);
+    if (get<uint32_t>(f.h, 96) != gdn_crc32c(0, buf.data(), buf.size()))
         return fail(GDN_ECORRUPT, "snapshot: payload checksum mismatch in %s", path);
     return GDN_OK;
 }
@@ -171,26 +198,9 @@ int hip_fail(const char* what, hipError_t e)
     return fail(GDN_EHIP, "snapshot: %s: %s", what, hipGetErrorString(e));
 }
 
-} // namespace
-
-extern "C" {
-
-uint32_t gdn_crc32c(uint32_t crc, const void* data, size_t len)
+int save(const gdn_pool* pool, int32_t slot, uint64_t key, int64_t position, const char* path,
+         gdn_stream_t stream)
 {
-    static const bool hw = __builtin_cpu_supports("sse4.2");
-    const uint8_t* p = static_cast<const uint8_t*>(data);
-    const uint32_t c = ~crc;
-    return ~(hw ? crc_hw(c, p, len) : crc_soft(c, p, len));
-}
-
-int gdn_snapshot_save(const gdn_pool* pool, int32_t slot, uint64_t key, int64_t position,
-                      const char* path, gdn_stream_t stream)
-{
-    gdn::clear_error();
-    if (!pool || !path)
-        return fail(GDN_EINVAL, "snapshot: NULL pool or path");
-    if (slot < 0 || slot >= pool->desc.num_slots)
-        return fail(GDN_ERANGE, "snapshot: slot %d out of range", slot);
     const Layout L = layout_of(pool);
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int64_t per = L.win + L.st;
@@ -233,27 +243,27 @@ int gdn_snapshot_save(const gdn_pool* pool, int32_t slot, uint64_t key, int64_t 
         unlink(tmp.c_str());
         return fail(GDN_EIO, "snapshot: cannot write %s", path);
     }
+    // make the rename itself durable: sync the directory that holds the file
+    const std::string p(path);
+    const size_t slash = p.rfind('/');
+    const std::string dir = slash == std::string::npos ? "." : (slash == 0 ? "/" : p.substr(0, slash));
+    const int dfd = open(dir.c_str(), O_RDONLY | O_DIRECTORY);
+    const bool synced = dfd >= 0 && fsync(dfd) == 0;
+    if (dfd >= 0)
+        close(dfd);
+    if (!synced)
+        return fail(GDN_EIO, "snapshot: %s written, but its directory could not be synced", path);
     return GDN_OK;
 }
 
-int gdn_snapshot_load(const gdn_pool* pool, int32_t slot, const char* path, uint64_t key,
-                      int64_t* position, int32_t drop_damaged, gdn_stream_t stream)
+int load(const gdn_pool* pool, int32_t slot, const char* path, uint64_t key, int64_t* position,
+         gdn_stream_t stream)
 {
-    gdn::clear_error();
-    if (!pool || !path || !position)
-        return fail(GDN_EINVAL, "snapshot: NULL argument");
-    if (slot < 0 || slot >= pool->desc.num_slots)
-        return fail(GDN_ERANGE, "snapshot: slot %d out of range", slot);
-    std::vector<uint8_t> buf;
-    int rc = read_checked(path, buf);
-    if (rc == GDN_ECORRUPT && drop_damaged) {
-        const std::string msg = gdn_last_error();
-        unlink(path);
-        return fail(GDN_ECORRUPT, "%s (file dropped)", msg.c_str());
-    }
+    File f;
+    int rc = open_checked(path, f);
     if (rc != GDN_OK)
         return rc;
-    const uint8_t* h = buf.data();
+    const uint8_t* h = f.h;
     const Layout L = layout_of(pool);
     const int32_t want[9] = {L.nl, L.C, L.W, L.Hk, L.Hv, L.dk, L.dv, 1, 2};
     for (int i = 0; i < 9; ++i)
@@ -263,12 +273,19 @@ int gdn_snapshot_load(const gdn_pool* pool, int32_t slot, const char* path, uint
         return fail(GDN_EINVAL, "snapshot: %s has other region sizes than the pool", path);
     if (get<uint64_t>(h, 16) != key)
         return fail(GDN_EINVAL, "snapshot: %s holds another key", path);
-    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int64_t per = L.win + L.st;
+    if (f.payload != per * L.nl)
+        return fail(GDN_ECORRUPT, "snapshot: %s states a payload of %lld bytes for this layout",
+                    path, (long long)f.payload);
+    std::vector<uint8_t> buf;
+    rc = read_payload(path, f, buf);
+    if (rc != GDN_OK)
+        return rc;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     for (int32_t i = 0; i < L.nl; ++i) {
         uint8_t* page = static_cast<uint8_t*>(pool->bases[pool->linear[i]]) +
                         int64_t(slot) * pool->desc.page_stride_bytes;
-        const uint8_t* src = buf.data() + kHeader + i * per;
+        const uint8_t* src = buf.data() + i * per; // buf holds the payload only
         hipError_t e = hipMemcpyAsync(page + pool->desc.conv_offset_bytes, src, size_t(L.win),
                                       hipMemcpyHostToDevice, s);
         if (e == hipSuccess && L.st > 0)
@@ -284,16 +301,17 @@ int gdn_snapshot_load(const gdn_pool* pool, int32_t slot, const char* path, uint
     return GDN_OK;
 }
 
-int gdn_snapshot_read_info(const char* path, gdn_snapshot_info* out)
+int read_info(const char* path, gdn_snapshot_info* out)
 {
-    gdn::clear_error();
-    if (!path || !out)
-        return fail(GDN_EINVAL, "snapshot: NULL argument");
-    std::vector<uint8_t> buf;
-    const int rc = read_checked(path, buf);
+    File f;
+    int rc = open_checked(path, f);
     if (rc != GDN_OK)
         return rc;
-    const uint8_t* h = buf.data();
+    std::vector<uint8_t> buf;
+    rc = read_payload(path, f, buf);
+    if (rc != GDN_OK)
+        return rc;
+    const uint8_t* h = f.h;
     out->key = get<uint64_t>(h, 16);
     out->position = get<int64_t>(h, 24);
     out->num_linear_layers = get<int32_t>(h, 32);
@@ -308,6 +326,57 @@ int gdn_snapshot_read_info(const char* path, gdn_snapshot_info* out)
     out->payload_bytes = get<int64_t>(h, 88);
     out->payload_crc = get<uint32_t>(h, 96);
     return GDN_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+uint32_t gdn_crc32c(uint32_t crc, const void* data, size_t len)
+{
+    static const bool hw = __builtin_cpu_supports("sse4.2");
+    const uint8_t* p = static_cast<const uint8_t*>(data);
+    const uint32_t c = ~crc;
+    return ~(hw ? crc_hw(c, p, len) : crc_soft(c, p, len));
+}
+
+int gdn_snapshot_save(const gdn_pool* pool, int32_t slot, uint64_t key, int64_t position,
+                      const char* path, gdn_stream_t stream)
+{
+    gdn::clear_error();
+    if (!pool || !path)
+        return fail(GDN_EINVAL, "snapshot: NULL pool or path");
+    if (slot < 0 || slot >= pool->desc.num_slots)
+        return fail(GDN_ERANGE, "snapshot: slot %d out of range", slot);
+    return gdn::guarded([&] { return save(pool, slot, key, position, path, stream); });
+}
+
+int gdn_snapshot_load(const gdn_pool* pool, int32_t slot, const char* path, uint64_t key,
+                      int64_t* position, int32_t drop_damaged, gdn_stream_t stream)
+{
+    gdn::clear_error();
+    if (!pool || !path || !position)
+        return fail(GDN_EINVAL, "snapshot: NULL argument");
+    if (slot < 0 || slot >= pool->desc.num_slots)
+        return fail(GDN_ERANGE, "snapshot: slot %d out of range", slot);
+    return gdn::guarded([&] {
+        const int rc = load(pool, slot, path, key, position, stream);
+        if (rc == GDN_ECORRUPT && drop_damaged) {
+            char msg[512];
+            snprintf(msg, sizeof msg, "%s", gdn_last_error());
+            unlink(path);
+            return fail(GDN_ECORRUPT, "%s (file dropped)", msg);
+        }
+        return rc;
+    });
+}
+
+int gdn_snapshot_read_info(const char* path, gdn_snapshot_info* out)
+{
+    gdn::clear_error();
+    if (!path || !out)
+        return fail(GDN_EINVAL, "snapshot: NULL argument");
+    return gdn::guarded([&] { return read_info(path, out); });
 }
 
 } // extern "C"

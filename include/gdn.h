@@ -70,7 +70,8 @@ enum {
     GDN_EOVERLAP = -3,          /* restore: duplicate dst, or a src that is also a dst */
     GDN_EALIGN = -4,            /* a pointer, offset or stride is not 16-byte aligned */
     GDN_EUNSUPPORTED = -5,      /* geometry without a compiled kernel variant */
-    GDN_EHIP = -6               /* the HIP runtime refused a launch */
+    GDN_EHIP = -6,              /* the HIP runtime refused a launch */
+    GDN_ENOMEM = -11            /* host memory exhausted (no C++ exception crosses the ABI) */
 };
 
 /* ---------------------------------------------------------------------- */

@@ -43,7 +43,10 @@
  * Errors: 0 (GDN_OK) or a negative GDN_E* code from gdn.h; GDN_ENOSLOT when
  * no slot can be found for a new sequence; GDN_ESTATE for a call out of
  * order (commit without resolve, resolve while a batch is pending).  A
- * failed call changes nothing.  gdn_last_error() gives the message.
+ * call that fails a check changes nothing.  When host memory runs out
+ * (GDN_ENOMEM; no C++ exception leaves the library) a resolve is rolled
+ * back like an abort, while a commit may have applied part of the batch.
+ * gdn_last_error() gives the message.
  * The manager is not thread-safe: one scheduler thread drives it.
  */
 #ifndef GDN_SLOTS_H

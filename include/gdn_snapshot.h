@@ -40,10 +40,17 @@
  * returning.  Host memory for the payload is allocated and freed inside the
  * call; no device memory is allocated.
  *
+ * Reading takes the 128-byte header first: a file that is not a snapshot,
+ * whose header checksum fails, or whose size is not the header's plus the
+ * payload the header states is rejected before any payload is read or
+ * memory for it is allocated.  Writing syncs the file, renames it, then
+ * syncs its directory.
+ *
  * Errors: GDN_EINVAL (NULL / bad argument, or a pool whose layout differs
  * from the file's), GDN_ERANGE (slot out of range), GDN_EIO (the file could
- * not be written / read), GDN_ECORRUPT (identity or checksum mismatch,
- * truncated file), GDN_EHIP (a copy failed).
+ * not be written / read / made durable), GDN_ECORRUPT (identity or checksum
+ * mismatch, truncated file, a payload size that does not fit the layout),
+ * GDN_EHIP (a copy failed), GDN_ENOMEM (host memory for the payload).
  */
 #ifndef GDN_SNAPSHOT_H
 #define GDN_SNAPSHOT_H

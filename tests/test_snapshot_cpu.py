@@ -93,3 +93,19 @@ def test_reader_rejects_truncated_and_extended_files(tmp_path):
     with pytest.raises(gdn.GdnError) as e:
         gdn.gdn_snapshot_read_info(str(tmp_path / "missing.bin"))
     assert e.value.code == gdn.GDN_EIO
+
+
+def test_reader_rejects_a_consistent_header_that_states_a_huge_payload(tmp_path):
+    """A header with a valid checksum whose payload size does not match the
+    file: rejected from the header and the file size alone (the reader must
+    not try to allocate the stated 2^62 bytes)."""
+    import struct
+    blob = bytearray(build_file(7, 16, LAYOUT, payload(4)))
+    struct.pack_into("<q", blob, 88, 1 << 62)
+    struct.pack_into("<I", blob, 100, crc32c(bytes(blob[:100])))
+    p = tmp_path / "s.bin"
+    p.write_bytes(bytes(blob))
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.gdn_snapshot_read_info(str(p))
+    assert e.value.code == gdn.GDN_ECORRUPT
+    assert "truncated" in str(e.value)

@@ -128,12 +128,12 @@ def dev(a):
     return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
 
 
-def bench_decode(steps, warmup):
+def bench_decode(steps, warmup, extra_pad=0):
     import torch
     import hybrid_linear_attention_slot_amd as gdn
     import workloads as wl
 
-    inp, pages = wl.decode_workload(seed=0)
+    inp, pages = wl.decode_workload(seed=0, extra_pad=extra_pad)
     g = inp.geom
     pool = torch.zeros((g.num_slots, g.page_stride), dtype=torch.uint8, device="cuda")
     idx = torch.from_numpy(inp.state_indices.astype(np.int64)).cuda()
@@ -356,6 +356,8 @@ def main():
         torch.cuda.empty_cache()
     inp, ms, nbytes, dpc = bench_decode(a.steps, a.warmup)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    _, ms_pad, nbytes_pad, _ = bench_decode(a.steps, a.warmup, extra_pad=4096)
+    torch.cuda.empty_cache()
     pinp, ppc, pms_ck = bench_prefill(a.steps, a.warmup)
     pms = ppc["p50"]
     pflops = prefill_flops(pinp) / (pms * 1e-3) / 1e12
@@ -392,6 +394,9 @@ def main():
         "warmup": a.warmup,
         "ms_per_step": round(ms, 5),
         "per_launch_us": {k: round(v * 1e3, 2) for k, v in dpc.items()},
+        "decode_4k_padded_pages": {"gb_per_s": round(nbytes_pad / (ms_pad * 1e-3) / 1e9, 2),
+                                   "ms_per_step": round(ms_pad, 5),
+                                   "note": "same step, 4 KiB of padding after every payload"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

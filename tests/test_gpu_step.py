@@ -231,12 +231,15 @@ def test_tiny_config_continuation_on_gpu():
                   "tiny decode continuation")
 
 
-def test_decode_full_shape_matches_oracle():
+@pytest.mark.parametrize("extra_pad", [0, 4096])
+def test_decode_full_shape_matches_oracle(extra_pad):
     """256 rows x 32 heads x 128x128 fp32, 1024-slot pool with 4 KiB pages,
-    90 % warm rows (the decode workload), all rows against the oracle."""
-    inp, pages = wl.decode_workload(seed=0)
+    90 % warm rows (the decode workload), all rows against the oracle; also
+    with 4 KiB of padding after each payload (a page stride that is no longer
+    the payload rounded up)."""
+    inp, pages = wl.decode_workload(seed=0, extra_pad=extra_pad)
     g = inp.geom
-    log("decode workload: filling 1024-slot pool")
+    log(f"decode workload (+{extra_pad} B padding): filling 1024-slot pool")
     gen = torch.Generator(device="cuda").manual_seed(1)
     pool = torch.randint(0, 256, (g.num_slots, g.page_stride), dtype=torch.uint8, device="cuda",
                          generator=gen)

@@ -3,7 +3,9 @@
 Argument marshalling only: every function forwards to the C-ABI entry point
 of the same name (include/gdn.h), which validates and enqueues gfx950 kernels
 on the given stream.  Device buffers may be given as torch tensors (their
-data_ptr() is used) or as integer addresses.  The library must have been
+data_ptr() is used; a tensor that is not a contiguous GPU tensor of the
+expected element size is refused here, before any kernel could read a host
+address) or as integer addresses, which are passed on unchecked.  The library must have been
 built (`python -m hybrid_linear_attention_slot_amd.build`); there is no
 fallback: loading fails loudly when libgdn.so is missing.
 """
@@ -163,11 +165,19 @@ def lib() -> C.CDLL:
     return _lib
 
 
-def _addr(t) -> Optional[int]:
+def _addr(t, elem: int = 0, name: str = "buffer") -> Optional[int]:
+    """Device address of `t`: None, an int (unchecked), or a torch tensor that
+    must be a contiguous GPU tensor (with `elem`-byte elements when elem > 0)."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got one on {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if elem and t.element_size() != elem:
+        raise ValueError(f"{name} must have {elem}-byte elements (got {t.dtype})")
     return int(t.data_ptr())
 
 
@@ -219,7 +229,8 @@ def gdn_pool_create(layer_base: Sequence, num_slots: int, page_stride_bytes: int
                     head_v_dim: int) -> Pool:
     """layer_base: per layer a device buffer (tensor or address) of num_slots
     pages, or None for an attention-only layer."""
-    bases = (C.c_void_p * len(layer_base))(*[_addr(b) for b in layer_base])
+    bases = (C.c_void_p * len(layer_base))(*[_addr(b, 0, f"layer_base[{i}]")
+                                             for i, b in enumerate(layer_base)])
     d = gdn_pool_desc(len(layer_base), C.cast(bases, C.POINTER(C.c_void_p)), num_slots,
                       page_stride_bytes, conv_offset_bytes, ssm_offset_bytes, conv_channels,
                       conv_width, num_k_heads, num_v_heads, head_k_dim, head_v_dim)
@@ -250,28 +261,33 @@ def gdn_restore_slots(pool: Pool, ops, has_initial_state, stream=None) -> int:
     Returns GDN_OK or GDN_WARN_COLD_FALLBACK."""
     ops = [tuple(int(v) for v in op) for op in ops]
     arr = (gdn_restore_op * max(1, len(ops)))(*[gdn_restore_op(*op) for op in ops])
-    return _check(lib().gdn_restore_slots(pool.handle, arr, len(ops), _addr(has_initial_state),
+    return _check(lib().gdn_restore_slots(pool.handle, arr, len(ops),
+                                          _addr(has_initial_state, 1, "has_initial_state"),
                                           _stream(stream)))
 
 
 def gdn_gather_states(pool: Pool, layer: int, idx, n: int, ssm_dense, conv_dense,
                       stream=None) -> int:
-    return _check(lib().gdn_gather_states(pool.handle, layer, _addr(idx), n, _addr(ssm_dense),
-                                          _addr(conv_dense), _stream(stream)))
+    return _check(lib().gdn_gather_states(pool.handle, layer, _addr(idx, 4, "idx"), n,
+                                          _addr(ssm_dense, 0, "ssm_dense"),
+                                          _addr(conv_dense, 0, "conv_dense"), _stream(stream)))
 
 
 def gdn_scatter_states(pool: Pool, layer: int, idx, n: int, ssm_dense, conv_dense,
                        stream=None) -> int:
-    return _check(lib().gdn_scatter_states(pool.handle, layer, _addr(idx), n, _addr(ssm_dense),
-                                           _addr(conv_dense), _stream(stream)))
+    return _check(lib().gdn_scatter_states(pool.handle, layer, _addr(idx, 4, "idx"), n,
+                                           _addr(ssm_dense, 0, "ssm_dense"),
+                                           _addr(conv_dense, 0, "conv_dense"), _stream(stream)))
 
 
 def make_step_args(x, conv_w, conv_b, alpha, beta, state_indices, has_initial_state, out,
                    scale=1.0, l2_eps=1e-6) -> gdn_step_args:
     """The returned struct keeps references to the tensors it names, so that
     temporaries passed here stay allocated as long as the struct lives."""
-    a = gdn_step_args(_addr(x), _addr(conv_w), _addr(conv_b), _addr(alpha), _addr(beta),
-                      _addr(state_indices), _addr(has_initial_state), _addr(out),
+    a = gdn_step_args(_addr(x, 2, "x"), _addr(conv_w, 2, "conv_w"), _addr(conv_b, 2, "conv_b"),
+                      _addr(alpha, 4, "alpha"), _addr(beta, 4, "beta"),
+                      _addr(state_indices, 4, "state_indices"),
+                      _addr(has_initial_state, 1, "has_initial_state"), _addr(out, 2, "out"),
                       float(scale), float(l2_eps))
     a._keep = (x, conv_w, conv_b, alpha, beta, state_indices, has_initial_state, out)
     return a
@@ -284,7 +300,8 @@ def gdn_decode_step(pool: Pool, layer: int, rows: int, args: gdn_step_args, stre
 
 def gdn_prefill_varlen(pool: Pool, layer: int, num_seqs: int, cu_seqlens, max_seqlen: int,
                        total_tokens: int, args: gdn_step_args, stream=None) -> int:
-    return _check(lib().gdn_prefill_varlen(pool.handle, layer, num_seqs, _addr(cu_seqlens),
+    return _check(lib().gdn_prefill_varlen(pool.handle, layer, num_seqs,
+                                           _addr(cu_seqlens, 4, "cu_seqlens"),
                                            max_seqlen, total_tokens, C.byref(args),
                                            _stream(stream)))
 
@@ -293,8 +310,9 @@ def gdn_prefill_varlen_checkpoint(pool: Pool, layer: int, num_seqs: int, cu_seql
                                   max_seqlen: int, total_tokens: int, args: gdn_step_args,
                                   ckpt_slot, ckpt_len, stream=None) -> int:
     return _check(lib().gdn_prefill_varlen_checkpoint(
-        pool.handle, layer, num_seqs, _addr(cu_seqlens), max_seqlen, total_tokens,
-        C.byref(args), _addr(ckpt_slot), _addr(ckpt_len), _stream(stream)))
+        pool.handle, layer, num_seqs, _addr(cu_seqlens, 4, "cu_seqlens"), max_seqlen,
+        total_tokens, C.byref(args), _addr(ckpt_slot, 4, "ckpt_slot"),
+        _addr(ckpt_len, 4, "ckpt_len"), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

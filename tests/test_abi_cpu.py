@@ -173,3 +173,42 @@ def test_gather_scatter_validation():
         gdn.gdn_scatter_states(p, 0, None, 2, FAKE, FAKE, stream=0)
     assert e.value.code == gdn.GDN_EINVAL
     assert gdn.gdn_gather_states(p, 0, FAKE, 0, FAKE, FAKE, stream=0) == gdn.GDN_OK
+
+
+class _FakeGpuTensor:
+    """Stands in for a GPU tensor in the binding's argument checks (no GPU here)."""
+    is_cuda = True
+    device = "cuda:0"
+
+    def __init__(self, elem, contiguous=True):
+        self._elem, self._contiguous = elem, contiguous
+        self.dtype = f"{elem}-byte"
+
+    def is_contiguous(self):
+        return self._contiguous
+
+    def element_size(self):
+        return self._elem
+
+    def data_ptr(self):
+        return 0x10000
+
+
+def test_binding_refuses_host_noncontiguous_and_wrong_width_tensors():
+    """A host tensor's address would reach a kernel as a device address: the
+    binding refuses it (and non-contiguous or wrong-width tensors) before any
+    call into the library."""
+    import torch
+    ok = dict(x=_FakeGpuTensor(2), conv_w=_FakeGpuTensor(2), conv_b=None,
+              alpha=_FakeGpuTensor(4), beta=_FakeGpuTensor(4),
+              state_indices=_FakeGpuTensor(4), has_initial_state=_FakeGpuTensor(1),
+              out=_FakeGpuTensor(2))
+    gdn.make_step_args(**ok)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gdn.make_step_args(**dict(ok, x=torch.zeros(8, dtype=torch.int16)))
+    with pytest.raises(ValueError, match="contiguous"):
+        gdn.make_step_args(**dict(ok, out=_FakeGpuTensor(2, contiguous=False)))
+    with pytest.raises(ValueError, match="4-byte"):
+        gdn.make_step_args(**dict(ok, alpha=_FakeGpuTensor(2)))
+    with pytest.raises(ValueError, match="1-byte"):
+        gdn.make_step_args(**dict(ok, has_initial_state=_FakeGpuTensor(4)))

@@ -297,32 +297,40 @@ def bench_slot_manager(rows=256, steps=200):
                     "and later ones match restores and skip saves for want of free slots"}
 
 
-def cpu_baseline(inp_decode, min_seconds=10.0):
-    """The oracle on this host, on the decode batch, repeated for >= min_seconds."""
+def cpu_baseline(inp_decode, min_seconds=10.0, single_thread_seconds=4.0):
+    """The oracle on this host, on the decode batch, repeated for >= min_seconds
+    with up to 16 threads, then for >= single_thread_seconds on one thread."""
     import dataclasses
 
     import oracle
     import workloads as wl
 
-    threads = min(os.cpu_count() or 1, 16)
-    oracle.set_threads(threads)
     _, pages = wl.decode_workload(seed=0)
     sub = dataclasses.replace(inp_decode.geom, num_slots=inp_decode.num_seqs)
     loc = np.arange(inp_decode.num_seqs, dtype=np.int32)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        work = pages.copy()
-        oracle.gdn_layer(work, sub, inp_decode.cu_seqlens, loc, inp_decode.has_initial_state,
-                         inp_decode.x, inp_decode.conv_w, inp_decode.conv_b, inp_decode.alpha,
-                         inp_decode.beta)
-        reps += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(decode_bytes(inp_decode) * reps / dt / 1e9, 4), "unit": "GB/s",
-            "cores": oracle.get_threads(), "kind": "oracle",
+
+    def run(threads, seconds):
+        oracle.set_threads(threads)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            work = pages.copy()
+            oracle.gdn_layer(work, sub, inp_decode.cu_seqlens, loc, inp_decode.has_initial_state,
+                             inp_decode.x, inp_decode.conv_w, inp_decode.conv_b,
+                             inp_decode.alpha, inp_decode.beta)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        return reps, time.perf_counter() - t0, oracle.get_threads()
+
+    reps, dt, cores = run(min(os.cpu_count() or 1, 16), min_seconds)
+    reps1, dt1, _ = run(1, single_thread_seconds)
+    nb = decode_bytes(inp_decode)
+    return {"value": round(nb * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
             "sample": f"the full decode batch (256 rows x 32 heads) x {reps} repetitions, "
-                      f"{dt:.1f} s, fp64 C oracle with OpenMP over rows"}
+                      f"{dt:.1f} s, fp64 C oracle with OpenMP over rows",
+            "single_thread_value": round(nb * reps1 / dt1 / 1e9, 4),
+            "single_thread_sample": f"{reps1} repetitions on 1 thread, {dt1:.1f} s"}
 
 
 def main():

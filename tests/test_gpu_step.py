@@ -155,6 +155,14 @@ def test_prefill_skips_sequences_outside_total_tokens():
     check_pages(g, got, ref, slots=inp.state_indices[:1], what="skipped sequences")
 
 
+def test_prefill_long_sequence():
+    """One sequence of 65,536 tokens (4,096 chunks) beside a short one: long
+    token loop, within the tolerance all the way."""
+    g = wl.make_geometry(4, Hk=1, Hv=2, dk=32, dv=32, W=4, page_align=128, extra_pad=128)
+    inp, img = case(g, 990, [65536, 3], [1, 0], bias=True)
+    run_and_check(g, inp, img, "prefill", "65536-token sequence")
+
+
 def test_prefill_many_short_sequences():
     """More sequences than one wave can rank (the placement by length then
     keeps the natural order), lengths 0..20 including many shorter than the

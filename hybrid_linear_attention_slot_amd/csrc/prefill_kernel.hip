@@ -220,6 +220,10 @@ void prefill_kernel(PrefillParams p)
 
     if (wave < NCONS) {
         // ======================= consumer waves =============================
+        // The recurrence is the critical path and each consumer shares its
+        // SIMD with a producer wave, which has a chunk of slack: when both can
+        // issue, the consumer goes first.
+        __builtin_amdgcn_s_setprio(3);
         const int col = wave * CPW + lane / LPC; // value column inside the slice
         const int jl = lane % LPC;
         const int gcol = sl * ISZ + col;
@@ -360,15 +364,22 @@ void prefill_kernel(PrefillParams p)
                 }
             };
             if (nt == CT && ck_tok / CT != c && quiet) {
-                // full chunk: a fixed-trip loop without branches, so that each
-                // token waits only for its own operands (the last fetch of the
-                // chunk re-reads token CT-1 and is unused)
+                // full chunk: a fully unrolled loop without branches (every LDS
+                // address is a base plus an immediate), in which the operands of
+                // token t+1 are requested before token t is computed; the
+                // scheduling barriers keep the compiler from sinking those reads
+                // next to their use, so each token waits only for reads issued
+                // a whole token earlier (the last fetch of the chunk re-reads
+                // token CT-1 and is unused)
                 constexpr std::false_type scaled{};
                 fetch(A, buf, 0, scaled);
+#pragma unroll
                 for (int tt = 0; tt < CT; tt += 2) {
                     fetch(B, buf, tt + 1, scaled);
+                    __builtin_amdgcn_sched_barrier(0);
                     step(A, buf, tt, scaled);
                     fetch(A, buf, min(tt + 2, CT - 1), scaled);
+                    __builtin_amdgcn_sched_barrier(0);
                     step(B, buf, tt + 1, scaled);
                 }
             } else if (quiet) { // a ragged last chunk, or the chunk holding the checkpoint token

@@ -10,28 +10,35 @@
 // scattered back into the same page ("非连续 KV Cache" §5-§6).
 //
 // Parallel structure.  Every value column of a head's state evolves on its
-// own once k, q, v, a, b of the token are known, so a workgroup takes one
+// own once k, v, a, b of the token are known, so a workgroup takes one
 // (sequence, v-head, slice of ISZ value columns) and keeps that slice of the
 // state in registers for the whole sequence.  Its waves have two roles:
-//   - consumer waves run the serial recurrence.  A lane holds KPL keys of one
-//     value column (keys 4 jl + 4 LPC m + e, so that the LPC lanes of a
-//     column read one contiguous run of k or q from LDS); S k and S q are
-//     lane-partial dot products finished with DPP sums over the LPC lanes,
-//     and  o = a (S_old q^) + d (k^.q^),  d = b (v - a S_old k^),  so one pass
-//     over the state gives both the update and the output;
+//   - consumer waves run the recurrence and nothing else.  A lane holds KPL
+//     keys of one value column (keys 4 jl + 4 LPC m + e, so that the LPC
+//     lanes of a column read one contiguous run of k from LDS); S k is a
+//     lane-partial dot product finished with DPP sums over the LPC lanes,
+//     d = b (v - a S_old k^) and S <- a S_old + d k^T.  A consumer writes d of
+//     every token, and the state at the start of every chunk, to LDS;
 //   - producer waves prepare the next chunk of CT tokens while the consumers
-//     work on the current one: they stage the raw inputs of the workgroup's
-//     channels (q and k of its k-head, v of its slice) in an LDS ring with
-//     coalesced 16-byte loads issued a chunk ahead, run the conv + SiLU, form
-//     the per-token norm factors, and write the previous chunk's outputs to
-//     HBM as bf16.
-// Consumers and producers meet at one barrier per chunk; the per-token work
-// on the critical path is the consumers' recurrence alone.  The L2 norm
-// factors are applied to the reduced sums, so k and q stay raw in LDS.
-// A run split at a multiple of the chunk length (16 tokens) and resumed from
-// the written-back state gives the same bits as the straight run: the state
-// is folded to its plain form at every chunk start, which is also the form
-// written back.
+//     work on the current one (raw inputs loaded into registers a chunk
+//     ahead, conv + SiLU, norm factors, decay products), and form the
+//     outputs of a chunk from what the consumers left, on the matrix cores.
+//     Within a chunk, with S_0 the state at its start, A_t the product of the
+//     chunk's decays through token t and D the chunk's d values,
+//         o_t = S_t q^_t = A_t S_0 q^_t + sum_{s<=t} (A_t / A_s) (k^_s . q^_t) d_s,
+//     i.e. per 16-column block O = alpha (S_0 Q^T) + D M^T with M the masked,
+//     decay-weighted 16x16 Q K^T of the chunk: three fp32 16x16x4 MFMA
+//     products per chunk (S_0 Q^T and Q K^T while the consumers run the
+//     chunk, D M^T after it).  The output is not on the recurrence's path, so
+//     this takes a third of the per-token work off the serial chain.
+// Consumers and producers meet at two barriers per chunk (one after the
+// consumers have written the chunk's starting state, one at its end).  The L2
+// norm factors are applied to reduced sums and coefficients, so k and q stay
+// raw in LDS.  A run split at a multiple of the chunk length (16 tokens) and
+// resumed from the written-back state gives the same bits as the straight
+// run: the state is folded to its plain form at every chunk start, which is
+// also the form written back, and a chunk's outputs depend only on that state
+// and the chunk's own inputs.
 //
 // The conv window is rewritten by a second small kernel after this one, so
 // that no workgroup of a sequence can overwrite the window another workgroup
@@ -56,20 +63,26 @@ struct PrefillShape {
     static constexpr int NSL = DV / ISZ;                            // workgroups per head
     static constexpr int NT = 64 * (NCONS + NPROD);
     static constexpr int CT = 16;                                   // tokens per chunk
-    static constexpr int RING = 3 * CT;                             // staged input rows
-    static constexpr int NCH = 2 * DK + ISZ;                        // channels: q | k | v slice
-    static constexpr int NPIECE = NCH / 8;                          // 16-byte pieces per row
-    static constexpr int QKP = DK / 2;                              // q (and k) channel pairs
-    static constexpr int NQK = (QKP + 63) / 64;                     // q/k pair slots per lane
-    static constexpr int NVP = ISZ / 2;                             // v channel pairs
-    static constexpr int PLANES = 64 * NPROD;
-    static constexpr int LOADS = (CT * NPIECE + PLANES - 1) / PLANES; // pieces per producer lane
-    static constexpr int OPR = ISZ / 8;                             // 8-column output pieces per row
-    static constexpr int TPW = CT / NPROD;                          // tokens per producer wave
+    static constexpr int YS = 2 * DK + ISZ + 4;   // conv outputs per token row (q|k|v slice|pad)
+    static constexpr int SROW = DK + 4;           // starting-state row (one value column), padded
+    static constexpr int NCB = ISZ / 16;          // 16-column output blocks
+    static constexpr int KQ = DK / 4;             // keys per MFMA lane group
+    static constexpr int QKP = DK / 2;            // q (and k) channel pairs
+    static constexpr int NVP = ISZ / 2;           // v channel pairs
+    static constexpr int TPW = CT / NPROD;        // tokens per producer wave
+    static constexpr int NVJ = (TPW * NVP + 63) / 64; // v conv jobs per producer lane
+    // Q K^T is split over the producer waves without an output block: GP
+    // parts of the key range (a power of two dividing the KQ / 4 steps)
+    static constexpr int GFREE = NPROD - NCB;
+    static constexpr int GP = (GFREE >= 4 && (KQ / 4) % 4 == 0) ? 4
+                            : (GFREE >= 2 && (KQ / 4) % 2 == 0) ? 2 : 1;
     static_assert(DK == DV, "square heads only");
     static_assert(KPL % 4 == 0 && DK % KPL == 0 && LPC >= 1 && LPC <= 64, "key split");
-    static_assert(NCONS >= 1 && DV % ISZ == 0 && ISZ % 8 == 0, "column split");
-    static_assert(CT == 16, "a chunk's decays are reduced over one 16-lane DPP row");
+    static_assert(NCONS >= 1 && DV % ISZ == 0 && ISZ % 16 == 0, "column split");
+    static_assert(CT == 16, "a chunk is one 16-wide MFMA tile and one 16-lane DPP row");
+    static_assert(NCB <= NPROD, "each producer wave keeps at most one output block");
+    static_assert(QKP <= 64, "one q/k channel pair per producer lane");
+    static_assert(KQ % 4 == 0, "MFMA operands are read as float4 runs");
 };
 
 struct PrefillParams {
@@ -97,6 +110,8 @@ struct PrefillParams {
     float scale;
     float eps;
 };
+
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float lo_bf16(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -132,11 +147,21 @@ __device__ __forceinline__ int seq_at_position(const int32_t* cu, int N, int r)
 constexpr uint32_t kFoldBelow = (127u - 40u) << 23;
 
 // A token's coefficients in LDS (floats):
-//   SC_SCALED  c rk, b, rk / c, c rq   (c: running product of the chunk's
-//                                      decays through the token)
-//   SC_KQ      k^.q^, c
-//   SC_PLAIN   a, b, rk, rq            (chunks that may need a fold)
-constexpr int SC_SCALED = 0, SC_KQ = 4, SC_PLAIN = 8;
+//   SC_SCALED  c rk, b, rk / c, c     (c: running product of the chunk's
+//                                     decays through the token)
+//   SC_PLAIN   a, b, rk, rq           (chunks that may need a fold)
+constexpr int SC_SCALED = 0, SC_PLAIN = 4, SC_N = 8;
+
+constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer resource, gfx9-family layout
+
+// A buffer resource's range from a wave-uniform byte count, capped at
+// INT32_MAX; kept in a scalar register so loads through it need no loop
+// over distinct resources.
+__device__ __forceinline__ int range_bytes(int64_t n)
+{
+    const int r = n > int64_t(INT32_MAX) ? INT32_MAX : int(n);
+    return __builtin_amdgcn_readfirstlane(r);
+}
 
 // v * (lane v of the row n lanes lower), or v * 1 for the first n lanes of
 // each 16-lane row (DPP row_shr; an invalid source keeps the `old` operand)
@@ -147,10 +172,9 @@ __device__ __forceinline__ float row_shr_or_one(float v)
                                                       0x110 + N, 0xF, 0xF, false));
 }
 
-template <int RING>
-__device__ __forceinline__ int ring_pos(int t) // t >= -RING
+__device__ __forceinline__ v4f mfma16(float a, float b, v4f c)
 {
-    return (t + RING) % RING;
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 template <int DK, int DV, int W>
@@ -160,15 +184,21 @@ void prefill_kernel(PrefillParams p)
 {
     using Sh = PrefillShape<DK, DV>;
     constexpr int KPL = Sh::KPL, LPC = Sh::LPC, CPW = Sh::CPW, NCONS = Sh::NCONS;
-    constexpr int ISZ = Sh::ISZ, NCH = Sh::NCH, CT = Sh::CT, RING = Sh::RING;
-    constexpr int NT = Sh::NT, PLANES = Sh::PLANES, NPIECE = Sh::NPIECE, QKP = Sh::QKP;
+    constexpr int ISZ = Sh::ISZ, CT = Sh::CT, YS = Sh::YS, SROW = Sh::SROW, NCB = Sh::NCB;
+    constexpr int KQ = Sh::KQ, QKP = Sh::QKP, NVP = Sh::NVP, TPW = Sh::TPW, NVJ = Sh::NVJ;
 
-    __shared__ __align__(16) uint16_t raw[RING][NCH];  // staged raw inputs, row = token % RING
-    __shared__ __align__(16) float ys[2][CT][NCH];     // conv outputs (raw q | raw k | v)
-    __shared__ __align__(16) float sc[2][CT][12];      // per token coefficients (SC_*)
-    __shared__ uint32_t nofold[2];                     // the chunk's decays need no fold
-    __shared__ __align__(8) float gab[RING][2];        // staged alpha, beta
-    __shared__ __align__(16) float ob[2][CT][ISZ];     // outputs of a chunk (fp32)
+    // Chunk k's inputs are written while chunk k-1 runs, read by the
+    // consumers and the products while it runs, and its coefficients once more
+    // by its epilogue while chunk k+1 runs, when chunk k+2 is being prepared:
+    // hence two buffers for the conv outputs and three for the coefficients.
+    __shared__ __align__(16) float ys[2][CT][YS];      // conv outputs (raw q | raw k | v)
+    __shared__ __align__(16) float s0[ISZ][SROW];      // the state at the current chunk's start
+    __shared__ __align__(16) float sc[3][CT][SC_N];    // per token coefficients (SC_*)
+    __shared__ __align__(16) float alf[3][CT];         // output scale A_t rq_t per token
+    __shared__ __align__(16) float dbuf[2][CT][ISZ];   // d per (token, value column)
+    __shared__ __align__(16) float gq[2][Sh::GP][CT][CT]; // parts of a chunk's Q K^T
+    __shared__ __align__(16) v4f pq[2][NCB][64];        // S_0 Q^T of a block, MFMA lane order
+    __shared__ uint32_t nofold[3];                     // the chunk's decays need no fold
 
     // workgroup -> (k-head g, dispatch position of sequence n, v-head of the
     // group, slice): the workgroups of one (n, g) read the same q/k inputs and
@@ -198,7 +228,7 @@ void prefill_kernel(PrefillParams p)
     uint16_t* out_base = p.out + int64_t(tb) * out_tok + int64_t(h) * DV + sl * ISZ;
     const int slot = p.state_indices[n];
     if (slot < 0 || slot >= p.num_slots) { // padding row: zero outputs, no state I/O
-        for (int e = tid; e < L * (ISZ / 4); e += NT) {
+        for (int e = tid; e < L * (ISZ / 4); e += Sh::NT) {
             const int tt = e / (ISZ / 4), c4 = e - tt * (ISZ / 4);
             *reinterpret_cast<uint2*>(out_base + tt * out_tok + 4 * c4) = make_uint2(0u, 0u);
         }
@@ -234,24 +264,24 @@ void prefill_kernel(PrefillParams p)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 s[4 * m + e] = warm ? tile[(4 * jl + 4 * LPC * m + e) * DV + gcol] : 0.f;
+        // d of tokens past a ragged chunk's end meets zeros in M; it must be
+        // finite, so the buffers start at zero
+        for (int e = tid; e < 2 * CT * ISZ; e += 64 * NCONS)
+            (&dbuf[0][0][0])[e] = 0.f;
         // operands of one token; the next token's are fetched from LDS while
         // the current one is computed
         struct Ops {
-            float4 k[KPL / 4], q[KPL / 4];
+            float4 k[KPL / 4];
             float4 g; // SC_SCALED or SC_PLAIN
-            float2 h; // k^.q^, running scale
             float v;
         };
-        auto fetch = [&](Ops& r, int buf, int tt, auto checked) {
+        auto fetch = [&](Ops& r, int buf, int sb, int tt, auto checked) {
             const float* yt = ys[buf][tt];
 #pragma unroll
-            for (int m = 0; m < KPL / 4; ++m) {
+            for (int m = 0; m < KPL / 4; ++m)
                 r.k[m] = *reinterpret_cast<const float4*>(yt + DK + 4 * jl + 4 * LPC * m);
-                r.q[m] = *reinterpret_cast<const float4*>(yt + 4 * jl + 4 * LPC * m);
-            }
             r.g = *reinterpret_cast<const float4*>(
-                &sc[buf][tt][decltype(checked)::value ? SC_PLAIN : SC_SCALED]);
-            r.h = *reinterpret_cast<const float2*>(&sc[buf][tt][SC_KQ]);
+                &sc[sb][tt][decltype(checked)::value ? SC_PLAIN : SC_SCALED]);
             r.v = yt[2 * DK + col];
         };
         // The state is held as cs * s: the decays of a chunk's tokens gather in
@@ -270,8 +300,8 @@ void prefill_kernel(PrefillParams p)
         // which they also fold into the token's coefficients.
         auto step = [&](const Ops& r, int buf, int tt, auto checked) {
             constexpr bool kChecked = decltype(checked)::value;
-            const float b = r.g.y, kq = r.h.x;
-            float ca, cu, rkc, cq; // a S_old = ca s; ca rk; rk / ca; ca rq
+            const float b = r.g.y;
+            float ca, cu, rkc; // a S_old = ca s; ca rk; rk / ca
             if constexpr (kChecked) {
                 ca = cs * r.g.x;
                 if ((__builtin_amdgcn_readfirstlane(__float_as_uint(ca)) & 0x7FFFFFFFu) <
@@ -281,28 +311,21 @@ void prefill_kernel(PrefillParams p)
                 }
                 cu = ca * r.g.z;
                 rkc = r.g.z * __builtin_amdgcn_rcpf(ca);
-                cq = ca * r.g.w;
             } else {
-                ca = r.h.y;
+                ca = r.g.w;
                 cu = r.g.x;
                 rkc = r.g.z;
-                cq = r.g.w;
             }
-            float u0 = 0.f, u1 = 0.f, o0 = 0.f, o1 = 0.f;
+            float u0 = 0.f, u1 = 0.f;
 #pragma unroll
             for (int m = 0; m < KPL / 4; ++m) {
                 u0 = fmaf(s[4 * m + 0], r.k[m].x, u0);
                 u1 = fmaf(s[4 * m + 1], r.k[m].y, u1);
-                o0 = fmaf(s[4 * m + 0], r.q[m].x, o0);
-                o1 = fmaf(s[4 * m + 1], r.q[m].y, o1);
                 u0 = fmaf(s[4 * m + 2], r.k[m].z, u0);
                 u1 = fmaf(s[4 * m + 3], r.k[m].w, u1);
-                o0 = fmaf(s[4 * m + 2], r.q[m].z, o0);
-                o1 = fmaf(s[4 * m + 3], r.q[m].w, o1);
             }
             const float u = group_sum<LPC>(u0 + u1); // s k (raw k)
-            const float o = group_sum<LPC>(o0 + o1); // s q (raw q)
-            const float d = b * (r.v - cu * u); // b (v - a S_old k^)
+            const float d = b * (r.v - cu * u);      // b (v - a S_old k^)
             // S <- a S_old + d k^ k^T = ca (s + (d rk / ca) k)
             const float dk = d * rkc;
 #pragma unroll
@@ -313,11 +336,10 @@ void prefill_kernel(PrefillParams p)
                 s[4 * m + 3] = fmaf(dk, r.k[m].w, s[4 * m + 3]);
             }
             cs = ca;
-            // a S_old q^ + d (k^.q^); the LPC lanes of the column hold the same
-            // bits (each step of group_sum adds the same two values in every
-            // lane), so all of them store it: no exec-mask switch per token
-            const float ov = fmaf(cq, o, kq * d);
-            ob[buf][tt][col] = ov;
+            // the LPC lanes of the column hold the same bits (each step of
+            // group_sum adds the same two values in every lane), so all of
+            // them store it: no exec-mask switch per token
+            dbuf[buf][tt][col] = d;
         };
         // checkpoint emission: the state after token ck_tok (if any) is also
         // stored into the checkpoint page
@@ -345,19 +367,24 @@ void prefill_kernel(PrefillParams p)
                         __float_as_uint(s[4 * m + e] * cs), ck_rs,
                         voff + (4 * LPC * m + e) * DV * 4, 0, 0);
         };
-        __syncthreads(); // A: history and chunk 0 staged
-        __syncthreads(); // B: chunk 0 prepared
+        __syncthreads(); // B: chunk 0 prepared, d buffers cleared
         for (int c = 0; c < nchunks; ++c) {
-            const int buf = c & 1;
+            const int buf = c & 1, sb = c % 3;
             const int nt = chunk_len(c);
             fold(cs);
             cs = 1.f;
+            // the chunk's starting state, for the producers' output products
+#pragma unroll
+            for (int m = 0; m < KPL / 4; ++m)
+                *reinterpret_cast<float4*>(&s0[col][4 * jl + 4 * LPC * m]) =
+                    make_float4(s[4 * m], s[4 * m + 1], s[4 * m + 2], s[4 * m + 3]);
+            __syncthreads(); // X: starting state written
             // the producers' verdict: no token of the chunk needs a fold
-            const bool quiet = __builtin_amdgcn_readfirstlane(nofold[buf]) != 0u;
+            const bool quiet = __builtin_amdgcn_readfirstlane(nofold[sb]) != 0u;
             Ops A, B;
             auto per_token = [&](auto checked) {
                 for (int tt = 0; tt < nt; ++tt) {
-                    fetch(A, buf, tt, checked);
+                    fetch(A, buf, sb, tt, checked);
                     step(A, buf, tt, checked);
                     if (c * CT + tt == ck_tok)
                         store_ck();
@@ -372,13 +399,13 @@ void prefill_kernel(PrefillParams p)
                 // a whole token earlier (the last fetch of the chunk re-reads
                 // token CT-1 and is unused)
                 constexpr std::false_type scaled{};
-                fetch(A, buf, 0, scaled);
+                fetch(A, buf, sb, 0, scaled);
 #pragma unroll
                 for (int tt = 0; tt < CT; tt += 2) {
-                    fetch(B, buf, tt + 1, scaled);
+                    fetch(B, buf, sb, tt + 1, scaled);
                     __builtin_amdgcn_sched_barrier(0);
                     step(A, buf, tt, scaled);
-                    fetch(A, buf, min(tt + 2, CT - 1), scaled);
+                    fetch(A, buf, sb, min(tt + 2, CT - 1), scaled);
                     __builtin_amdgcn_sched_barrier(0);
                     step(B, buf, tt + 1, scaled);
                 }
@@ -387,7 +414,7 @@ void prefill_kernel(PrefillParams p)
             } else {
                 per_token(std::true_type{});
             }
-            __syncthreads();
+            __syncthreads(); // P: chunk done
         }
 #pragma unroll
         for (int m = 0; m < KPL / 4; ++m)
@@ -398,15 +425,13 @@ void prefill_kernel(PrefillParams p)
     }
 
     // ========================= producer waves ===============================
-    const int pw = wave - NCONS;
-    const int plane = pw * 64 + lane;
+    const int pw = wave - Sh::NCONS;
     const uint16_t* win = reinterpret_cast<const uint16_t*>(page + p.conv_off);
 
     // conv taps and bias of the lane's channel pairs: q and k pair `lane`
-    // (lanes past DK/2 idle), v pair `lane % NVP` of the slice
-    static_assert(Sh::NQK == 1 && 64 % Sh::NVP == 0, "one q/k pair per lane; v pairs tile a wave");
-    float wq[2][W], wk[2][W], wv[2][W];
-    float bq[2], bk[2], bv[2];
+    // (lanes past DK/2 idle), v pair of each of the lane's v jobs
+    float wq[2][W], wk[2][W], wv[NVJ][2][W];
+    float bq[2], bk[2], bv[NVJ][2];
     auto load_taps = [&](int ch, float (&w2)[2][W], float (&b2)[2]) {
         const int c = chan(ch);
 #pragma unroll
@@ -418,133 +443,146 @@ void prefill_kernel(PrefillParams p)
         }
     };
     const int qkp = min(lane, QKP - 1); // q/k pair of the lane (clamped; idle lanes recompute)
-    const int vp = lane % Sh::NVP;      // v pair of the lane
     load_taps(2 * qkp, wq, bq);
     load_taps(DK + 2 * qkp, wk, bk);
-    load_taps(2 * DK + 2 * vp, wv, bv);
+    // v job jj of the lane: token t0 + vi[jj] of the wave's TPW, pair vpj[jj]
+    int vi[NVJ], vpj[NVJ];
+#pragma unroll
+    for (int jj = 0; jj < NVJ; ++jj) {
+        const int j = lane + 64 * jj;
+        vi[jj] = j / NVP;
+        vpj[jj] = j % NVP;
+        load_taps(2 * DK + 2 * vpj[jj], wv[jj], bv[jj]);
+    }
 
-    // chunk k's raw rows and gates: issue (into registers), then stage (to LDS).
-    // Every lane issues the same number of 16-byte loads whatever the chunk's
-    // length (pieces past the last token re-read the last token's row and land
-    // in ring rows no conv reads), so the waits for them are exact.
-    // (a native vector type: an array of HIP's uint4 is kept in scratch memory
-    // here, which turns the prefetch into a load, a wait and a spill)
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 pf[Sh::LOADS];
+    // Raw inputs of chunk k for this wave's TPW tokens, loaded into registers
+    // a chunk ahead: for q and k the lane's channel pair over the W-1 rows
+    // before the wave's first token and its TPW rows; for v the W rows of each
+    // job; the gates of token k CT + lane % CT.  All are buffer loads with the
+    // row in the lane's offset: the range check returns zero for rows past
+    // the sequence's end (their results are never stored) and for the rows
+    // before its start when the sequence is cold, whose window resource is
+    // empty, so no load waits on a branch and a cold page is never read.
+    constexpr int HR = W - 1, NR = HR + TPW;
+    constexpr uint32_t kOutOfRange = 0xFFFFFFF0u; // past any num_records below
+    const int t0 = pw * TPW;
+    uint32_t xq[NR], xk[NR], xv[NVJ][W];
     float2 pg;
+    // byte offsets inside a row of x of the lane's q pair, k pair, and (from
+    // the wave's first row) of each v job's first row
+    const int rowb = p.C * 2;
+    const int oq = chan(2 * qkp) * 2, ok = chan(DK + 2 * qkp) * 2;
+    int ov[NVJ];
+#pragma unroll
+    for (int jj = 0; jj < NVJ; ++jj)
+        ov[jj] = min(vi[jj], TPW - 1) * rowb + chan(2 * DK + 2 * vpj[jj]) * 2;
+    auto ld = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0);
+    };
     auto issue = [&](int k) {
         if (k >= nchunks)
             return;
-        const int last = chunk_len(k) - 1;
+        const int rbase = k * CT + t0 - HR; // the wave's first row
+        // the first of its rows inside the sequence; L (an empty range) when
+        // the wave's tokens all lie past the end of a short last chunk
+        const int xb = min(max(rbase, 0), L);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(p.x) + int64_t(tb + xb) * p.C, short(0),
+            range_bytes(int64_t(L - xb) * rowb), kBufferWord3);
+        if (rbase >= 0) {
 #pragma unroll
-        for (int i = 0; i < Sh::LOADS; ++i) {
-            const int e = min(plane + PLANES * i, CT * NPIECE - 1);
-            const int tt = e / NPIECE, pc = e - tt * NPIECE;
-            pf[i] = *reinterpret_cast<const u32x4*>(p.x + int64_t(tb + k * CT + min(tt, last)) * p.C +
-                                                   chan(8 * pc));
-        }
-        const int64_t gi = int64_t(tb + k * CT + min(plane % CT, last)) * p.Hv + h;
-        pg = make_float2(p.alpha[gi], p.beta[gi]);
-    };
-    auto stage = [&](int k) {
-        if (k >= nchunks)
-            return;
-#pragma unroll
-        for (int i = 0; i < Sh::LOADS; ++i) {
-            const int e = plane + PLANES * i;
-            if (e < CT * NPIECE) {
-                const int tt = e / NPIECE, pc = e - tt * NPIECE;
-                *reinterpret_cast<u32x4*>(&raw[ring_pos<RING>(k * CT + tt)][8 * pc]) = pf[i];
+            for (int i = 0; i < NR; ++i) {
+                xq[i] = ld(rs, oq + i * rowb);
+                xk[i] = ld(rs, ok + i * rowb);
             }
-        }
-        if (plane < CT)
-            *reinterpret_cast<float2*>(gab[ring_pos<RING>(k * CT + plane)]) = pg;
-    };
-
-    // conv + SiLU and the norm factors of chunk k into ys[k & 1], sc[k & 1].
-    // Producer wave pw takes the TPW consecutive tokens starting at pw * TPW.
-    // For q and k each lane walks them in order for its channel pair, keeping
-    // the W-1 previous inputs in registers (primed from the ring), so every
-    // staged input is unpacked once; the v channels of the slice are fewer
-    // than the lanes, so there a lane takes one (token, pair) job and reads
-    // its window from the ring.  The 3 TPW wave sums (|q|^2, |k|^2, q.k of
-    // each token) are reduced together, and lane i finishes the coefficients
-    // of the wave's i-th token.
-    auto prepare = [&](int k) {
-        constexpr int TPW = Sh::TPW;
-        static_assert(TPW == 4, "the sums of 4 tokens are reduced together");
-        const int buf = k & 1;
-        const int t0 = pw * TPW;
-        const int t1 = min(t0 + TPW, chunk_len(k));
-        if (t0 >= t1)
-            return;
-        const int base = (k % 3) * CT; // ring row of the chunk's first token
-        auto row = [&](int tt) {       // tt in [-(W-1), CT)
-            const int r = base + tt;
-            return reinterpret_cast<const uint32_t*>(raw[r < 0 ? r + RING : r]);
-        };
-        // v: job j = lane + 64 jj is token t0 + j / NVP, pair vp
 #pragma unroll
-        for (int jj = 0; jj < (TPW * Sh::NVP + 63) / 64; ++jj) {
-            const int i = (lane + 64 * jj) / Sh::NVP;
-            const int tt = t0 + i;
-            if (i < TPW && tt < t1) {
-                float a0 = bv[0], a1 = bv[1];
+            for (int jj = 0; jj < NVJ; ++jj)
+#pragma unroll
+                for (int w = 0; w < W; ++w)
+                    xv[jj][w] = ld(rs, ov[jj] + w * rowb);
+        } else {
+            // the first chunk of wave 0: rows -HR .. -1 come from the window
+            const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(win), short(0), warm ? HR * rowb : 0, kBufferWord3);
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int r = i - HR; // rbase == -HR here
+                xq[i] = r < 0 ? ld(rw, (HR + r) * rowb + oq) : ld(rs, r * rowb + oq);
+                xk[i] = r < 0 ? ld(rw, (HR + r) * rowb + ok) : ld(rs, r * rowb + ok);
+            }
+#pragma unroll
+            for (int jj = 0; jj < NVJ; ++jj) {
+                const int cv = chan(2 * DK + 2 * vpj[jj]) * 2;
 #pragma unroll
                 for (int w = 0; w < W; ++w) {
-                    const uint32_t xv = row(tt - (W - 1) + w)[2 * QKP + vp];
-                    a0 = fmaf(wv[0][w], lo_bf16(xv), a0);
-                    a1 = fmaf(wv[1][w], hi_bf16(xv), a1);
+                    const int r = min(vi[jj], TPW - 1) + w - HR;
+                    xv[jj][w] = ld(rw, r < 0 ? uint32_t((HR + r) * rowb + cv) : kOutOfRange) |
+                                ld(rs, r >= 0 ? uint32_t(r * rowb + cv) : kOutOfRange);
                 }
-                *reinterpret_cast<float2*>(ys[buf][tt] + 2 * DK + 2 * vp) =
+            }
+        }
+        // gates of token k CT + lane % CT (zero past the sequence's end)
+        const int ht = p.Hv * 4;
+        const int64_t g0 = int64_t(tb + k * CT) * p.Hv + h;
+        const int grec = range_bytes(int64_t(L - k * CT) * ht);
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(p.alpha) + g0, short(0), grec, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(p.beta) + g0, short(0), grec, kBufferWord3);
+        pg = make_float2(__uint_as_float(ld(ra, (lane % CT) * ht)),
+                         __uint_as_float(ld(rb, (lane % CT) * ht)));
+    };
+
+    // conv + SiLU, norm factors and coefficients of chunk k into ys[k & 1],
+    // sc[k % 3], alf[k % 3] and nofold[k % 3], for the wave's tokens
+    // [t0, t0 + TPW).  The 2 TPW wave sums (|q|^2, |k|^2 of each token) are
+    // reduced together, and lane i finishes the coefficients of the wave's
+    // i-th token.
+    auto prepare = [&](int k) {
+        static_assert(TPW == 4, "the sums of 4 tokens are reduced together");
+        if (k >= nchunks)
+            return;
+        const int buf = k & 1, sb = k % 3;
+        const int nt = chunk_len(k);
+        // v: one (token, pair) job per lane
+#pragma unroll
+        for (int jj = 0; jj < NVJ; ++jj) {
+            const int tt = t0 + vi[jj];
+            if (vi[jj] < TPW && tt < nt) {
+                float a0 = bv[jj][0], a1 = bv[jj][1];
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    a0 = fmaf(wv[jj][0][w], lo_bf16(xv[jj][w]), a0);
+                    a1 = fmaf(wv[jj][1][w], hi_bf16(xv[jj][w]), a1);
+                }
+                *reinterpret_cast<float2*>(&ys[buf][tt][2 * DK + 2 * vpj[jj]]) =
                     make_float2(silu(a0), silu(a1));
             }
         }
-        // q, k
-        float hq[2][W - 1], hk[2][W - 1];
-#pragma unroll
-        for (int w = 0; w < W - 1; ++w) {
-            const uint32_t* r = row(t0 - (W - 1) + w);
-            const uint32_t xq = r[qkp], xk = r[QKP + qkp];
-            hq[0][w] = lo_bf16(xq);
-            hq[1][w] = hi_bf16(xq);
-            hk[0][w] = lo_bf16(xk);
-            hk[1][w] = hi_bf16(xk);
-        }
-        // conv of one channel: taps over the W-1 held inputs and the current one,
-        // then the held inputs shift by one
-        auto conv1 = [&](const float (&wt)[W], float b, float (&hist)[W - 1], float x) {
+        // q, k: the lane walks the wave's tokens over its register rows
+        auto conv1 = [&](const float (&wt)[W], float b, const uint32_t (&xr)[NR], int i, bool hi) {
             float acc = b;
 #pragma unroll
-            for (int w = 0; w < W - 1; ++w)
-                acc = fmaf(wt[w], hist[w], acc);
-            acc = fmaf(wt[W - 1], x, acc);
-#pragma unroll
-            for (int w = 0; w + 1 < W - 1; ++w)
-                hist[w] = hist[w + 1];
-            hist[W - 2] = x;
+            for (int w = 0; w < W; ++w)
+                acc = fmaf(wt[w], hi ? hi_bf16(xr[i + w]) : lo_bf16(xr[i + w]), acc);
             return silu(acc);
         };
-        float sq[TPW], sk[TPW], qk[TPW];
+        float sq[TPW], sk[TPW];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-            sq[i] = sk[i] = qk[i] = 0.f;
+            sq[i] = sk[i] = 0.f;
             const int tt = t0 + i;
-            if (tt >= t1)
+            if (tt >= nt)
                 break;
-            const uint32_t* r = row(tt);
-            float* yt = ys[buf][tt];
-            const uint32_t xq = r[qkp], xk = r[QKP + qkp];
-            const float q0 = conv1(wq[0], bq[0], hq[0], lo_bf16(xq));
-            const float q1 = conv1(wq[1], bq[1], hq[1], hi_bf16(xq));
-            const float k0 = conv1(wk[0], bk[0], hk[0], lo_bf16(xk));
-            const float k1 = conv1(wk[1], bk[1], hk[1], hi_bf16(xk));
+            const float q0 = conv1(wq[0], bq[0], xq, i, false);
+            const float q1 = conv1(wq[1], bq[1], xq, i, true);
+            const float k0 = conv1(wk[0], bk[0], xk, i, false);
+            const float k1 = conv1(wk[1], bk[1], xk, i, true);
             if (lane < QKP) {
-                *reinterpret_cast<float2*>(yt + 2 * lane) = make_float2(q0, q1);
-                *reinterpret_cast<float2*>(yt + DK + 2 * lane) = make_float2(k0, k1);
+                *reinterpret_cast<float2*>(&ys[buf][tt][2 * lane]) = make_float2(q0, q1);
+                *reinterpret_cast<float2*>(&ys[buf][tt][DK + 2 * lane]) = make_float2(k0, k1);
                 sq[i] = fmaf(q0, q0, q1 * q1);
                 sk[i] = fmaf(k0, k0, k1 * k1);
-                qk[i] = fmaf(q0, k0, q1 * k1);
             }
         }
         // wave sums: halves (tokens 0|1 and 2|3 share a register), then rows
@@ -562,17 +600,16 @@ void prefill_kernel(PrefillParams p)
         auto token_sums = [&](const float (&v)[TPW]) {
             return group_sum<16>(fold_rows(fold_halves(v[0], v[1]), fold_halves(v[2], v[3])));
         };
-        const float tsq = token_sums(sq), tsk = token_sums(sk), tqk = token_sums(qk);
+        const float tsq = token_sums(sq), tsk = token_sums(sk);
         const int src = 16 * (((lane & 1) << 1) | ((lane >> 1) & 1)); // row of token lane & 3
-        const float my_sq = __shfl(tsq, src, 64), my_sk = __shfl(tsk, src, 64),
-                    my_qk = __shfl(tqk, src, 64);
-        // running products of the chunk's decays: an inclusive scan over lanes
-        // 0..15 (one DPP row; lanes past the chunk's end take 1).  Whether the
-        // state's scale can stay unfolded through the chunk: every decay in
-        // [0, 1] and their product at least 2^-40, so that no running product
-        // falls below it (NaN fails the test).
-        const int ntk = chunk_len(k);
-        const float av = lane < ntk ? gab[base + lane][0] : 1.f;
+        const float my_sq = __shfl(tsq, src, 64), my_sk = __shfl(tsk, src, 64);
+        // running products of the chunk's decays: an inclusive scan over each
+        // 16-lane row (lane i of a row: token i; lanes past the chunk's end
+        // take 1).  Whether the state's scale can stay unfolded through the
+        // chunk: every decay in [0, 1] and their product at least 2^-40, so
+        // that no running product falls below it (NaN fails the test).
+        const int ti = lane % CT;
+        const float av = ti < nt ? pg.x : 1.f;
         float cp = av;
         cp *= row_shr_or_one<1>(cp);
         cp *= row_shr_or_one<2>(cp);
@@ -583,61 +620,134 @@ void prefill_kernel(PrefillParams p)
             const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cp), 15));
             const bool quiet = __ballot(!ok) == 0 && total >= __uint_as_float(kFoldBelow);
             if (lane == 0)
-                nofold[buf] = quiet ? 1u : 0u;
+                nofold[sb] = quiet ? 1u : 0u;
         }
-        const float ct = __shfl(cp, min(t0 + lane, 15), 64); // running product through token t0+lane
-        const int tt = t0 + lane;
-        if (lane < TPW && tt < t1) {
-            const float rq = p.scale / sqrtf(my_sq + p.eps);
-            const float rk = 1.0f / sqrtf(my_sk + p.eps);
-            const float2 ab = *reinterpret_cast<const float2*>(gab[base + tt]);
-            float* o = sc[buf][tt];
+        const int tt = t0 + (lane & 3);
+        const float ct = __shfl(cp, tt, 64); // running product through token tt
+        const float ga = __shfl(pg.x, tt, 64), gb = __shfl(pg.y, tt, 64);
+        if (lane < TPW && tt < nt) {
+            const float rq = p.scale * __builtin_amdgcn_rsqf(my_sq + p.eps);
+            const float rk = __builtin_amdgcn_rsqf(my_sk + p.eps);
+            float* o = sc[sb][tt];
             *reinterpret_cast<float4*>(o + SC_SCALED) =
-                make_float4(ct * rk, ab.y, rk * __builtin_amdgcn_rcpf(ct), ct * rq);
-            *reinterpret_cast<float2*>(o + SC_KQ) = make_float2(my_qk * rq * rk, ct);
-            *reinterpret_cast<float4*>(o + SC_PLAIN) = make_float4(ab.x, ab.y, rk, rq);
+                make_float4(ct * rk, gb, rk * __builtin_amdgcn_rcpf(ct), ct);
+            *reinterpret_cast<float4*>(o + SC_PLAIN) = make_float4(ga, gb, rk, rq);
+            alf[k % 3][tt] = ct * rq;
         }
     };
 
-    // chunk k's outputs from ob[k & 1] to HBM as bf16
-    auto flush = [&](int k) {
+    // Output products of chunk k, while the consumers run it: producer wave
+    // j < NCB forms S_0 Q^T for the slice's j-th 16-column block (to LDS for
+    // the epilogue), the others form the GP parts of Q K^T over
+    // slices of the key range (to LDS; a single part goes to wave 0 when no
+    // wave is free).  MFMA lane l supplies A[l % 16][l / 16] and
+    // B[l / 16][l % 16] and receives D[4 (l / 16) + r][l % 16] in r; the K
+    // index of a step is permuted so that lane group l / 16 reads one run of
+    // consecutive keys.
+    constexpr int GP = Sh::GP;
+    const int m16 = lane % 16, q4 = lane / 16;
+    auto product = [&](const float* arow, const float* brow, int ngroups) {
+        // four independent accumulation chains keep the matrix pipe busy
+        v4f ac[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                     {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int i = 0; i < ngroups; ++i) {
+            const float4 a = *reinterpret_cast<const float4*>(arow + 4 * i);
+            const float4 b = *reinterpret_cast<const float4*>(brow + 4 * i);
+            ac[0] = mfma16(a.x, b.x, ac[0]);
+            ac[1] = mfma16(a.y, b.y, ac[1]);
+            ac[2] = mfma16(a.z, b.z, ac[2]);
+            ac[3] = mfma16(a.w, b.w, ac[3]);
+        }
+        return (ac[0] + ac[1]) + (ac[2] + ac[3]);
+    };
+    auto products = [&](int k) {
         const int buf = k & 1;
-        const int nt = chunk_len(k);
-        for (int e = plane; e < nt * Sh::OPR; e += PLANES) {
-            const int tt = e / Sh::OPR, c8 = e - tt * Sh::OPR;
-            const float4 lo = *reinterpret_cast<const float4*>(&ob[buf][tt][8 * c8]);
-            const float4 hi = *reinterpret_cast<const float4*>(&ob[buf][tt][8 * c8 + 4]);
-            const uint2 a = pack_bf16x4(lo.x, lo.y, lo.z, lo.w);
-            const uint2 b = pack_bf16x4(hi.x, hi.y, hi.z, hi.w);
-            *reinterpret_cast<uint4*>(out_base + int64_t(k * CT + tt) * out_tok + 8 * c8) =
-                make_uint4(a.x, a.y, b.x, b.y);
+        if (pw < NCB) // S_0[col][key] x Q[t][key], for the block's epilogue
+            pq[buf][pw][lane] = product(&s0[16 * pw + m16][q4 * KQ], &ys[buf][m16][q4 * KQ], KQ / 4);
+        const int gpart = Sh::GFREE > 0 ? pw - NCB : (pw == 0 ? 0 : -1);
+        if (gpart >= 0 && gpart < GP) { // Q[t][key] x K[s][key] over a slice of the keys
+            constexpr int NG = KQ / 4 / GP;
+            const int k0 = q4 * KQ + 4 * NG * gpart;
+            const v4f g4 = product(&ys[buf][m16][k0], &ys[buf][m16][DK + k0], NG);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                gq[buf][gpart][4 * q4 + r][m16] = g4[r];
         }
     };
 
-    // prologue: the W-1 inputs before the first token (window or zeros), chunk 0
-    for (int e = plane; e < (W - 1) * NCH; e += PLANES) {
-        const int w = e / NCH, ch = e - w * NCH;
-        raw[ring_pos<RING>(w - (W - 1))][ch] = warm ? win[int64_t(w) * p.C + chan(ch)] : uint16_t(0);
-    }
+    // Outputs of chunk k (after it): o = alf_t (S_0 Q^T) + D M^T for the
+    // wave's column block, written as bf16 (a lane: 4 columns of token l % 16).
+    // M[t][s] = (A_t / A_s) rq_t rk_s (q_t . k_s) for s <= t, else 0; chunks
+    // without a fold take A_t rq_t (alf) and rk_s / A_s (SC_SCALED), the
+    // others multiply the decays between s and t one by one.  A lane builds
+    // the B operand it supplies, M[t = l % 16][s = 4 (l / 16) + j], j = 0..3.
+    auto epilogue = [&](int k) {
+        // block eb of the chunk; on the waves without a block when there are
+        // enough of them (they carry the lighter products), else the block's own
+        const int eb = Sh::GFREE >= NCB ? pw - (Sh::NPROD - NCB) : pw;
+        if (eb < 0 || eb >= NCB)
+            return;
+        const int buf = k & 1, sb = k % 3;
+        const int t_ = m16;
+        float4 gsum = *reinterpret_cast<const float4*>(&gq[buf][0][t_][4 * q4]);
+#pragma unroll
+        for (int j = 1; j < GP; ++j) {
+            const float4 e = *reinterpret_cast<const float4*>(&gq[buf][j][t_][4 * q4]);
+            gsum.x += e.x;
+            gsum.y += e.y;
+            gsum.z += e.z;
+            gsum.w += e.w;
+        }
+        const float gs[4] = {gsum.x, gsum.y, gsum.z, gsum.w};
+        const float at = alf[k % 3][t_];
+        const bool quiet = __builtin_amdgcn_readfirstlane(nofold[sb]) != 0u;
+        float f[4];
+        if (quiet) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                f[j] = at * sc[sb][4 * q4 + j][SC_SCALED + 2];
+        } else {
+            // the decays between s and t, one token at a time (rare)
+            f[0] = f[1] = f[2] = f[3] = 1.f;
+#pragma unroll 1
+            for (int u = 1; u < CT; ++u) {
+                const float au = sc[sb][u][SC_PLAIN];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    f[j] *= (u > 4 * q4 + j && u <= t_) ? au : 1.f;
+            }
+            const float rq = sc[sb][t_][SC_PLAIN + 3];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                f[j] *= rq * sc[sb][4 * q4 + j][SC_PLAIN + 2];
+        }
+        v4f acc = pq[buf][eb][lane] * at;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s_ = 4 * q4 + j;
+            acc = mfma16(dbuf[buf][s_][16 * eb + m16], s_ <= t_ ? gs[j] * f[j] : 0.f, acc);
+        }
+        if (m16 < chunk_len(k)) {
+            *reinterpret_cast<uint2*>(out_base + int64_t(k * CT + m16) * out_tok + 16 * eb + 4 * q4) =
+                pack_bf16x4(acc[0], acc[1], acc[2], acc[3]);
+        }
+    };
+
     issue(0);
-    stage(0);
-    __syncthreads(); // A
-    issue(1);
     prepare(0);
-    stage(1);
+    issue(1);
     __syncthreads(); // B
     for (int c = 0; c < nchunks; ++c) {
-        // the loads are consumed by stage() after prepare(); the output stores
-        // go last, so that no wait for loads also waits for fresh stores
-        issue(c + 2);
-        if (c + 1 < nchunks)
-            prepare(c + 1);
-        stage(c + 2);
+        __syncthreads(); // X: the consumers have written the chunk's starting state
         if (c >= 1)
-            flush(c - 1);
-        __syncthreads();
+            epilogue(c - 1);
+        products(c);
+        prepare(c + 1);
+        issue(c + 2);
+        __syncthreads(); // P
     }
-    flush(nchunks - 1);
+    epilogue(nchunks - 1);
 }
 
 // Final window of each sequence: the last W-1 entries of (old window, x).

@@ -54,7 +54,7 @@ namespace {
 
 template <int DK, int DV>
 struct PrefillShape {
-    static constexpr int KPL = DK >= 64 ? 16 : (DK >= 32 ? 8 : 4); // keys per consumer lane
+    static constexpr int KPL = DK >= 128 ? 16 : (DK >= 32 ? 8 : 4); // keys per consumer lane
     static constexpr int LPC = DK / KPL;                            // lanes sharing one column
     static constexpr int CPW = 64 / LPC;                            // columns per consumer wave
     static constexpr int NCONS = (DV / CPW) < 4 ? (DV / CPW) : 4;   // consumer waves

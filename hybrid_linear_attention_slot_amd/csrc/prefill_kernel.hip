@@ -250,10 +250,8 @@ void prefill_kernel(PrefillParams p)
 
     if (wave < NCONS) {
         // ======================= consumer waves =============================
-        // The recurrence is the critical path and each consumer shares its
-        // SIMD with a producer wave, which has a chunk of slack: when both can
-        // issue, the consumer goes first.
-        __builtin_amdgcn_s_setprio(3);
+        // (each consumer shares its SIMD with a producer wave; the two roles'
+        // work per chunk is balanced, so neither takes issue priority)
         const int col = wave * CPW + lane / LPC; // value column inside the slice
         const int jl = lane % LPC;
         const int gcol = sl * ISZ + col;

@@ -343,11 +343,12 @@ int prefill_common(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
                     d.head_v_dim, d.conv_width);
     if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0)
         return GDN_OK;
-    if (!aligned16(a->x) || !aligned16(a->out))
-        return fail(GDN_EALIGN, "prefill: x and out must be 16-byte aligned");
-    if ((reinterpret_cast<uintptr_t>(a->conv_w) & 3u) != 0 ||
+    if ((reinterpret_cast<uintptr_t>(a->out) & 7u) != 0)
+        return fail(GDN_EALIGN, "out must be 8-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(a->x) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(a->conv_w) & 3u) != 0 ||
         (reinterpret_cast<uintptr_t>(a->conv_b) & 3u) != 0)
-        return fail(GDN_EALIGN, "conv_w and conv_b must be 4-byte aligned");
+        return fail(GDN_EALIGN, "x, conv_w and conv_b must be 4-byte aligned");
     return gdn::launch_prefill(pool, layer, num_seqs, total_tokens, cu_seqlens, a, ckpt_slot,
                                ckpt_len, reinterpret_cast<hipStream_t>(stream));
 }

@@ -192,8 +192,8 @@ int gdn_decode_step(const gdn_pool* pool, int32_t layer, int32_t rows,
  * synchronisation; the kernels skip a sequence whose range is empty or not
  * inside [0, total_tokens): no memory access, its slot and output rows are
  * left as they were).  max_seqlen is an upper bound of the lengths (host
- * hint).  A zero-length sequence leaves its slot untouched.  Alignment: x and out 16-byte aligned (the inputs are read
- * and the outputs written in 16-byte pieces), conv_w and conv_b 4-byte
+ * hint).  A zero-length sequence leaves its slot untouched.  Alignment as
+ * for gdn_decode_step: x, conv_w and conv_b 4-byte aligned, out 8-byte
  * aligned.  Errors as for gdn_decode_step. */
 int gdn_prefill_varlen(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
                        const int32_t* cu_seqlens_dev, int32_t max_seqlen, int64_t total_tokens,

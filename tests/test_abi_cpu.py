@@ -142,7 +142,7 @@ def test_step_validation():
     with pytest.raises(gdn.GdnError) as e:
         gdn.gdn_decode_step(p, 0, 4, step_args(conv_w=FAKE + 2), stream=0)
     assert e.value.code == gdn.GDN_EALIGN
-    for over in (dict(x=FAKE + 8), dict(out=FAKE + 8)):
+    for over in (dict(x=FAKE + 2), dict(out=FAKE + 4), dict(conv_b=FAKE + 2)):
         with pytest.raises(gdn.GdnError) as e:
             gdn.gdn_prefill_varlen(p, 0, 2, FAKE, 8, 16, step_args(**over), stream=0)
         assert e.value.code == gdn.GDN_EALIGN

@@ -10,7 +10,7 @@ import hybrid_linear_attention_slot_amd as gdn
 import oracle
 import workloads as wl
 from gpu_util import (DevicePool, check_outputs, check_pages, log, run_decode, run_prefill,
-                      u16)
+                      step_tensors, u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -129,6 +129,31 @@ def test_prefill_extreme_decays_match_oracle(d):
     o_2 = u16(t_2["out"]).reshape(2, 32, g.Hv, g.dv)
     assert np.array_equal(o_2, o_s[:, 32:]), "split run differs from the straight run"
     assert np.array_equal(a.host(), b.host()), "split run's pages differ"
+
+
+def test_prefill_word_aligned_inputs():
+    """x only 4-byte and out only 8-byte aligned (views into larger buffers),
+    with the last sequence's rows ending exactly at the end of x's buffer and
+    short last chunks, so that some producer waves of a last chunk have no
+    token inside the sequence: every input row read must still lie inside it."""
+    g = wl.make_geometry(8, Hk=2, Hv=4, dk=128, dv=128, W=4, page_align=128, extra_pad=128)
+    inp, img = case(g, 990, [37, 19, 3], [1, 0, 1], bias=True)
+    t = step_tensors(inp)
+    xb = torch.empty(t["x"].numel() + 2, dtype=t["x"].dtype, device="cuda")
+    xb[2:].copy_(t["x"].reshape(-1))
+    t["x"] = xb[2:].view(t["x"].shape)
+    ob = torch.full((t["out"].numel() + 4,), 0x7FC0, dtype=torch.int16, device="cuda")
+    t["out"] = ob[4:].view(t["out"].shape)
+    assert t["x"].data_ptr() % 16 == 4 and t["out"].data_ptr() % 16 == 8
+    dp = DevicePool(g, [img])
+    log(f"word-aligned prefill T={inp.total_tokens}")
+    run_prefill(dp, 0, inp, t)
+    torch.cuda.synchronize()
+    ref = img.copy()
+    o64, _ = oracle_layer(ref, inp)
+    check_outputs(u16(t["out"]), o64, "word-aligned prefill")
+    check_pages(g, dp.host(), ref, slots=inp.state_indices, what="word-aligned prefill")
+    assert (ob[:4] == 0x7FC0).all(), "write before out"
 
 
 def test_prefill_skips_sequences_outside_total_tokens():

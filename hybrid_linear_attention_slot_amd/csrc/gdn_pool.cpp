@@ -63,15 +63,17 @@ int check_layer(const gdn_pool* pool, int32_t layer)
     return GDN_OK;
 }
 
-int check_step_args(const gdn_pool* pool, int32_t layer, const gdn_step_args* a)
+// `work` is false for a call that reads and writes nothing (no rows, or no
+// tokens): its buffers may then be NULL, as empty tensors are.
+int check_step_args(const gdn_pool* pool, int32_t layer, const gdn_step_args* a, bool work)
 {
     int rc = check_layer(pool, layer);
     if (rc != GDN_OK)
         return rc;
     if (a == nullptr)
         return fail(GDN_EINVAL, "args is NULL");
-    if (!a->x || !a->conv_w || !a->alpha || !a->beta || !a->state_indices ||
-        !a->has_initial_state || !a->out)
+    if (work && (!a->x || !a->conv_w || !a->alpha || !a->beta || !a->state_indices ||
+                 !a->has_initial_state || !a->out))
         return fail(GDN_EINVAL, "a required device pointer in args is NULL");
     if (pool->desc.num_v_heads == 0)
         return fail(GDN_EUNSUPPORTED, "conv-window-only pool has no recurrent state");
@@ -304,7 +306,7 @@ int gdn_decode_step(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn
         return fail(GDN_EINVAL, "pool is NULL");
     if (rows < 0)
         return fail(GDN_EINVAL, "rows < 0");
-    int rc = check_step_args(pool, layer, a);
+    int rc = check_step_args(pool, layer, a, rows > 0);
     if (rc != GDN_OK)
         return rc;
     const gdn_pool_desc& d = pool->desc;
@@ -332,16 +334,17 @@ int prefill_common(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
         return fail(GDN_EINVAL, "pool is NULL");
     if (num_seqs < 0 || max_seqlen < 0 || total_tokens < 0)
         return fail(GDN_EINVAL, "negative num_seqs / max_seqlen / total_tokens");
-    int rc = check_step_args(pool, layer, a);
+    const bool work = num_seqs > 0 && total_tokens > 0 && max_seqlen > 0;
+    int rc = check_step_args(pool, layer, a, work);
     if (rc != GDN_OK)
         return rc;
-    if (!cu_seqlens)
+    if (work && !cu_seqlens)
         return fail(GDN_EINVAL, "cu_seqlens is NULL");
     const gdn_pool_desc& d = pool->desc;
     if (!gdn::prefill_supported(d.head_k_dim, d.head_v_dim, d.conv_width))
         return fail(GDN_EUNSUPPORTED, "no prefill kernel for dk=%d dv=%d W=%d", d.head_k_dim,
                     d.head_v_dim, d.conv_width);
-    if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0)
+    if (!work)
         return GDN_OK;
     if ((reinterpret_cast<uintptr_t>(a->out) & 7u) != 0)
         return fail(GDN_EALIGN, "out must be 8-byte aligned");
@@ -370,7 +373,7 @@ int gdn_prefill_varlen_checkpoint(const gdn_pool* pool, int32_t layer, int32_t n
                                   gdn_stream_t stream)
 {
     gdn::clear_error();
-    if (!ckpt_slot_dev || !ckpt_len_dev)
+    if ((!ckpt_slot_dev || !ckpt_len_dev) && num_seqs > 0 && total_tokens > 0 && max_seqlen > 0)
         return fail(GDN_EINVAL, "ckpt_slot and ckpt_len must not be NULL");
     return prefill_common(pool, layer, num_seqs, cu_seqlens, max_seqlen, total_tokens, a,
                           ckpt_slot_dev, ckpt_len_dev, stream);

@@ -177,7 +177,8 @@ typedef struct {
  * Row r uses slot state_indices[r]; when has_initial_state[r] == 0 the
  * window and state are taken as zero and the page is not read.  The updated
  * window and state are written back into the same page.  All pointers in
- * `args` are device pointers (conv_b may be NULL).  rows == 0 is a no-op.
+ * `args` are device pointers (conv_b may be NULL).  rows == 0 is a no-op
+ * that reads no buffer (they may then be NULL, as empty tensors are).
  * Alignment: x, conv_w and conv_b 4-byte aligned, out 8-byte aligned.
  * Errors: GDN_EINVAL (NULL pointer, rows < 0), GDN_ERANGE (layer out of
  * range or attention-only), GDN_EUNSUPPORTED (head dims), GDN_EALIGN. */
@@ -192,7 +193,9 @@ int gdn_decode_step(const gdn_pool* pool, int32_t layer, int32_t rows,
  * synchronisation; the kernels skip a sequence whose range is empty or not
  * inside [0, total_tokens): no memory access, its slot and output rows are
  * left as they were).  max_seqlen is an upper bound of the lengths (host
- * hint).  A zero-length sequence leaves its slot untouched.  Alignment as
+ * hint).  A zero-length sequence leaves its slot untouched.  A call with
+ * num_seqs, total_tokens or max_seqlen zero is a no-op whose buffers may be
+ * NULL (cu_seqlens_dev and the checkpoint arrays included).  Alignment as
  * for gdn_decode_step: x, conv_w and conv_b 4-byte aligned, out 8-byte
  * aligned.  Errors as for gdn_decode_step. */
 int gdn_prefill_varlen(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
@@ -208,7 +211,7 @@ int gdn_prefill_varlen(const gdn_pool* pool, int32_t layer, int32_t num_seqs,
  * window and state after its first ckpt_len_dev[n] tokens (payload only;
  * padding untouched); other values mean no checkpoint for that sequence.
  * ckpt_slot_dev, ckpt_len_dev: device int32 [num_seqs], both non-NULL
- * (GDN_EINVAL).  A checkpoint slot must differ from every state_indices
+ * unless the call is a no-op (GDN_EINVAL).  A checkpoint slot must differ from every state_indices
  * entry and from the other checkpoint slots of the call (not checkable on
  * the host; two writers of one page race).  Everything else as
  * gdn_prefill_varlen, whose results it leaves unchanged. */

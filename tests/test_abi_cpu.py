@@ -149,6 +149,18 @@ def test_step_validation():
     # zero rows / zero tokens are no-ops that launch nothing
     assert gdn.gdn_decode_step(p, 0, 0, a, stream=0) == gdn.GDN_OK
     assert gdn.gdn_prefill_varlen(p, 0, 0, FAKE, 0, 0, a, stream=0) == gdn.GDN_OK
+    # ... and may name no buffer at all (empty tensors have no address)
+    none = gdn.make_step_args(*[None] * 8)
+    assert gdn.gdn_decode_step(p, 0, 0, none, stream=0) == gdn.GDN_OK
+    assert gdn.gdn_prefill_varlen(p, 0, 3, None, 0, 0, none, stream=0) == gdn.GDN_OK
+    assert gdn.gdn_prefill_varlen_checkpoint(p, 0, 0, None, 0, 0, none, None, None,
+                                             stream=0) == gdn.GDN_OK
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.gdn_prefill_varlen(p, 0, 2, None, 8, 16, a, stream=0)
+    assert e.value.code == gdn.GDN_EINVAL
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.gdn_prefill_varlen_checkpoint(p, 0, 2, FAKE, 8, 16, a, None, FAKE, stream=0)
+    assert e.value.code == gdn.GDN_EINVAL
 
 
 def test_step_unsupported_geometry():

@@ -297,6 +297,36 @@ def bench_slot_manager(rows=256, steps=200):
                     "and later ones match restores and skip saves for want of free slots"}
 
 
+def bench_copy(reps=10):
+    """Context for the HBM-bound rows: torch's device-to-device copy of 1 GiB
+    (read + write bytes counted), median of per-call events."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    st = torch.cuda.current_stream()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    pc = per_call(lambda: dst.copy_(src), reps, st)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gb_per_s": round(2 * n / (pc["p50"] * 1e-3) / 1e9, 2), "bytes_per_call": 2 * n,
+            "what": "torch copy_ of a 1 GiB device buffer (read + write), median of "
+                    f"{reps} per-call events"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp_decode, min_seconds=10.0, single_thread_seconds=4.0):
     """The oracle on this host, on the decode batch, repeated for >= min_seconds
     with up to 16 threads, then for >= single_thread_seconds on one thread."""
@@ -326,7 +356,7 @@ def cpu_baseline(inp_decode, min_seconds=10.0, single_thread_seconds=4.0):
     reps1, dt1, _ = run(1, single_thread_seconds)
     nb = decode_bytes(inp_decode)
     return {"value": round(nb * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"the full decode batch (256 rows x 32 heads) x {reps} repetitions, "
                       f"{dt:.1f} s, fp64 C oracle with OpenMP over rows",
             "single_thread_value": round(nb * reps1 / dt1 / 1e9, 4),
@@ -421,6 +451,7 @@ def main():
         "prefill": prefill,
         "restore": restore,
     }
+    line["copy_baseline"] = bench_copy()
     line["slot_manager"] = bench_slot_manager()
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)

@@ -68,7 +68,7 @@ enum {
     GDN_EINVAL = -1,            /* bad argument (NULL, negative size, ...) */
     GDN_ERANGE = -2,            /* slot / layer / size out of range */
     GDN_EOVERLAP = -3,          /* restore: duplicate dst, or a src that is also a dst */
-    GDN_EALIGN = -4,            /* a pointer, offset or stride is not 16-byte aligned */
+    GDN_EALIGN = -4,            /* a pointer, offset or stride breaks the alignment its call states */
     GDN_EUNSUPPORTED = -5,      /* geometry without a compiled kernel variant */
     GDN_EHIP = -6,              /* the HIP runtime refused a launch */
     GDN_ENOMEM = -11            /* host memory exhausted (no C++ exception crosses the ABI) */

@@ -5,7 +5,8 @@ method's arithmetic (no conv, no norm, no delta rule, no copy semantics).
 Both the CPU oracle and the HIP path consume what it produces, so the two
 sides always see the same bytes.
 
-Distributions (see the workload recipe in the design doc for the reasoning):
+Distributions (the configurations fix x, alpha and beta; the rest is a plain
+choice of scale):
   x (pre-conv mixed q|k|v input)   ~ N(0, 1), rounded to bf16
   conv weights                     ~ U(-1/2, 1/2), bf16, layout [C][W]
   conv bias (optional)             ~ U(-1/2, 1/2), bf16

@@ -232,12 +232,34 @@ def bench_restore(steps, warmup):
     timed(call, 1, max(1, warmup), stream)
     ms = per_call(call, max(2, steps), stream)["p50"]
     hits = int((ops[:, 1] >= 0).sum())
-    nbytes = 2 * hits * int(linear.sum()) * (g.ssm_region_bytes + g.conv_region_bytes)
-    snap = bench_snapshot(h, int(ops[0, 0]), int(ops[1, 0]),
-                          int(linear.sum()) * (g.ssm_region_bytes + g.conv_region_bytes))
+    payload = g.ssm_region_bytes + g.conv_region_bytes
+    nbytes = 2 * hits * int(linear.sum()) * payload
+    # gather / scatter of the 64 op rows' pages on every GDN layer (one launch
+    # per layer, 48 launches per timed call)
+    idx = torch.from_numpy(np.ascontiguousarray(ops[:, 0])).cuda()
+    n = idx.numel()
+    ssm = torch.empty((n, g.ssm_region_bytes), dtype=torch.uint8, device="cuda")
+    conv = torch.empty((n, g.conv_region_bytes), dtype=torch.uint8, device="cuda")
+    layers = [l for l, lin in enumerate(linear) if lin]
+    gather = lambda: [gdn.gdn_gather_states(h, l, idx, n, ssm, conv, stream)  # noqa: E731
+                      for l in layers]
+    scatter = lambda: [gdn.gdn_scatter_states(h, l, idx, n, ssm, conv, stream)  # noqa: E731
+                       for l in layers]
+    gs_bytes = 2 * n * len(layers) * payload
+    gs = {}
+    for name, fn in (("gather", gather), ("scatter", scatter)):
+        timed(fn, 1, 1, stream)
+        gms = per_call(fn, 5, stream)["p50"]
+        gs[name] = {"gb_per_s": round(gs_bytes / (gms * 1e-3) / 1e9, 2), "ms_per_call": round(gms, 4),
+                    "frac_of_hbm_peak": round(gs_bytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    gs["bytes"] = gs_bytes
+    gs["what"] = f"{n} pages of each of the {len(layers)} GDN layers to dense rows and back " \
+                 "(one launch per layer, median of 5 per-call events over all layers)"
+    del ssm, conv
+    snap = bench_snapshot(h, int(ops[0, 0]), int(ops[1, 0]), int(linear.sum()) * payload)
     del bufs
     torch.cuda.empty_cache()
-    return ms, nbytes, hits, int(linear.sum()), snap
+    return ms, nbytes, hits, int(linear.sum()), snap, gs
 
 
 def bench_snapshot(pool, slot_a, slot_b, payload, reps=3):
@@ -417,11 +439,12 @@ def main():
     prefill["heads_32"] = bench_prefill_32heads(a.steps, a.warmup)
     restore = None
     if not a.no_restore:
-        rms, rbytes, hits, nlin, snap = bench_restore(a.steps, a.warmup)
+        rms, rbytes, hits, nlin, snap, gs = bench_restore(a.steps, a.warmup)
         restore = {"gb_per_s": round(rbytes / (rms * 1e-3) / 1e9, 2), "ms_per_call": round(rms, 4),
                    "bytes": rbytes, "hits": hits, "gdn_layers": nlin,
                    "frac_of_hbm_peak": round(rbytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                    "timing": "median of per-call HIP event pairs",
+                   "gather_scatter": gs,
                    "snapshot_one_slot": snap}
     line = {
         "metric": METRIC,

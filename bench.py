@@ -37,25 +37,30 @@ METRIC = "GDN decode state GB/s (% HBM peak) + prefill tokens/s, 32 heads x 128x
 def decode_bytes(inp) -> int:
     """Algorithmic bytes of one decode step: state read for warm rows and
     written for all rows, window read (warm) and written, x, alpha, beta,
-    output, conv weights, state index and flag."""
+    output, conv weights (and bias), state index and flag."""
     g = inp.geom
     B = inp.num_seqs
     n_w = int(inp.has_initial_state.sum())
     tile = g.Hv * g.dk * g.dv * 4
     win = (g.W - 1) * g.C * 2
+    bias = g.C * 2 if inp.conv_b is not None else 0
     return (n_w * tile + B * tile + n_w * win + B * win + B * g.C * 2 + B * g.Hv * 8
-            + B * g.Hv * g.dv * 2 + g.C * g.W * 2 + 5 * B)
+            + B * g.Hv * g.dv * 2 + g.C * g.W * 2 + bias + 5 * B)
 
 
 def prefill_bytes(inp) -> int:
+    """Algorithmic bytes of one varlen prefill: x, alpha, beta and output of
+    every token, each sequence's state and window read (warm) and written,
+    conv weights (and bias), slot index, flag and the n + 1 offsets."""
     g = inp.geom
     T = inp.total_tokens
     n = inp.num_seqs
     n_w = int(inp.has_initial_state.sum())
     tile = g.Hv * g.dk * g.dv * 4
     win = (g.W - 1) * g.C * 2
+    bias = g.C * 2 if inp.conv_b is not None else 0
     return (T * g.C * 2 + T * g.Hv * 8 + T * g.Hv * g.dv * 2 + (n_w + n) * (tile + win)
-            + g.C * g.W * 2 + 9 * n)
+            + g.C * g.W * 2 + bias + 9 * n + 4)
 
 
 DECODE_SOURCES = ("hybrid_linear_attention_slot_amd/csrc/decode_kernel.hip",

@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak (packed FMA)
+FP32_NONPACKED_PEAK_TFLOPS = 78.6  # the same without packed FMA, which this build does not emit
 
 METRIC = "GDN decode state GB/s (% HBM peak) + prefill tokens/s, 32 heads x 128x128 fp32"
 
@@ -435,6 +436,7 @@ def main():
                "gb_per_s": round(prefill_bytes(pinp) / (pms * 1e-3) / 1e9, 2),
                "tflops": round(pflops, 2),
                "frac_of_fp32_vector_peak": round(pflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+               "frac_of_fp32_nonpacked_peak": round(pflops / FP32_NONPACKED_PEAK_TFLOPS, 4),
                "workload": "8 seqs, lengths U{512..4096}, 16 v-heads/8 k-heads, 128x128 fp32, "
                            "4 warm + 4 cold",
                "ms_per_call_with_checkpoints": round(pms_ck, 4),

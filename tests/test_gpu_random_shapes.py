@@ -8,9 +8,11 @@ import numpy as np
 import pytest
 import torch
 
+import hybrid_linear_attention_slot_amd as gdn
 import oracle
 import workloads as wl
-from gpu_util import DevicePool, check_outputs, check_pages, log, run_decode, run_prefill, u16
+from gpu_util import (DevicePool, check_outputs, check_pages, log, run_decode, run_prefill,
+                      to_dev, u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,3 +60,81 @@ def test_random_configuration_matches_oracle(seed, decode):
         check_outputs(u16(t["out"]), o64, what)
     valid = [int(s) for s in inp.state_indices if 0 <= s < g.num_slots]
     check_pages(g, dp.host(), ref, slots=valid, what=what)
+
+
+def window_first_geometry(r, num_slots=20):
+    """A page with the window region first, then the state region, with gaps
+    (multiples of 16 bytes) before, between and after them."""
+    d = int(r.choice([32, 64, 128]))
+    Hk = int(r.integers(1, 3))
+    Hv = Hk * int(r.integers(1, 4))
+    W = int(r.integers(2, 5))
+    C = 2 * Hk * d + Hv * d
+    conv_off = 16 * int(r.integers(0, 9))
+    ssm_off = wl.round_up(conv_off + (W - 1) * C * 2, 16) + 16 * int(r.integers(0, 9))
+    stride = wl.round_up(ssm_off + Hv * d * d * 4, 16) + 16 * int(r.integers(0, 17))
+    return wl.Geometry(num_slots=num_slots, C=C, W=W, Hk=Hk, Hv=Hv, dk=d, dv=d,
+                       page_stride=stride, ssm_off=ssm_off, conv_off=conv_off)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_window_first_layout_matches_oracle(seed):
+    """Decode, prefill, restore, gather and scatter on pages whose window region
+    comes first and whose regions are separated by gaps: every kernel takes the
+    region offsets from the pool descriptor."""
+    r = np.random.default_rng(500 + seed)
+    g = window_first_geometry(r)
+    rng = wl.rng_for(20_000 + seed)
+    slots = r.permutation(g.num_slots).astype(np.int32)
+    live, ckpt = slots[:6], slots[6:10]
+    warm = np.array([1, 0, 1, 1, 0, 1], np.uint8)
+    img = wl.make_pool_image(g, rng, warm_slots=np.concatenate([live[warm == 1], ckpt]),
+                             nan_slots=live[warm == 0], sigma_s=0.5)
+    what = (f"seed {seed}: window-first page d={g.dk} Hk={g.Hk} Hv={g.Hv} W={g.W} "
+            f"conv_off={g.conv_off} ssm_off={g.ssm_off} stride={g.page_stride}")
+    log(what)
+    dp = DevicePool(g, [img])
+    ref = img.copy()
+    # restore two checkpoints into the first two rows (their pages become warm)
+    ops = np.array([[int(live[0]), int(ckpt[0]), 1], [int(live[1]), int(ckpt[1]), 1]], np.int32)
+    hs = torch.zeros(2, dtype=torch.uint8, device="cuda")
+    assert gdn.gdn_restore_slots(dp.pool, ops.tolist(), hs) == gdn.GDN_OK
+    hs_ref = np.zeros(2, np.uint8)
+    oracle.restore([ref], g, ops, hs_ref)
+    warm = warm.copy()
+    warm[:2] = hs_ref
+    dinp = wl.step_inputs(g, rng, [1] * 6, live, warm, bias=True)
+    td = run_decode(dp, 0, dinp)
+    pinp = wl.step_inputs(g, rng, [19, 1, 40, 16, 3, 0], live, np.ones(6, np.uint8),
+                          conv=(dinp.conv_w, dinp.conv_b))
+    tp = run_prefill(dp, 0, pinp)
+    # gather the live pages, scatter them onto the checkpoint slots shifted by one
+    gidx = live[:4].copy()
+    sidx = np.roll(ckpt, 1).astype(np.int32)
+    ssm = torch.empty((4, g.ssm_region_bytes), dtype=torch.uint8, device="cuda")
+    conv = torch.empty((4, g.conv_region_bytes), dtype=torch.uint8, device="cuda")
+    gdn.gdn_gather_states(dp.pool, 0, to_dev(gidx), 4, ssm, conv)
+    gdn.gdn_scatter_states(dp.pool, 0, to_dev(sidx), 4, ssm, conv)
+    torch.cuda.synchronize()
+    assert np.array_equal(hs.cpu().numpy(), hs_ref)
+    od, _ = oracle.gdn_layer(ref, g, dinp.cu_seqlens, live, warm, dinp.x, dinp.conv_w,
+                             dinp.conv_b, dinp.alpha, dinp.beta, dinp.scale, dinp.eps)
+    op, _ = oracle.gdn_layer(ref, g, pinp.cu_seqlens, live, pinp.has_initial_state, pinp.x,
+                             pinp.conv_w, pinp.conv_b, pinp.alpha, pinp.beta, pinp.scale,
+                             pinp.eps)
+    check_outputs(u16(td["out"]), od, what + " decode")
+    check_outputs(u16(tp["out"]), op, what + " prefill")
+    got = dp.host()
+    # the gathered rows are the GPU's own live pages: the dense copies must be
+    # exactly their payloads, and the scatter must put exactly those bytes
+    gs, gc = oracle.gather(got, g, gidx)
+    assert np.array_equal(ssm.cpu().numpy(), gs) and np.array_equal(conv.cpu().numpy(), gc)
+    oracle.scatter(ref, g, sidx, gs, gc)
+    # pages the steps touched: within tolerance of the oracle; the rest bit-exact
+    check_pages(g, got, ref, slots=np.concatenate([live, ckpt]), what=what)
+    for s in ckpt:  # scattered pages hold the GPU's gathered bytes exactly
+        pay = np.ones(g.page_stride, bool)
+        pay[:g.conv_off] = False
+        pay[g.conv_off + g.conv_region_bytes:g.ssm_off] = False
+        pay[g.ssm_off + g.ssm_region_bytes:] = False
+        assert np.array_equal(got[s][~pay], img[s][~pay]), what + ": gap or padding bytes changed"

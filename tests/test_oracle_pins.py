@@ -368,17 +368,17 @@ def test_layer_matches_product_form(Hk, Hv, dk, dv, bias, scale, eps):
     ref = product_form_layer(ref_pool, g, inp)
     scale_o = np.abs(ref).max()
     assert scale_o > 1e-3
-    np.testing.assert_allclose(o64, ref, rtol=0, atol=1e-6 * scale_o)
+    # both sides are fp64 and differ only in rounding order: ~1e-13 element-wise
+    np.testing.assert_allclose(o64, ref, rtol=1e-12, atol=1e-14 * scale_o)
     assert np.array_equal(o16, torch_bf16_bits(o64.astype(np.float32)))
-    # windows and padding bit-exact, states close
+    # windows, padding and the fp32 state words bit-exact (the two fp64 forms
+    # land on the same fp32 rounding of every state entry)
     for s in range(g.num_slots):
         a, b = img[s], ref_pool[s]
         cw = slice(g.conv_off, g.conv_off + g.conv_region_bytes)
         assert np.array_equal(a[cw], b[cw])
         pad = slice(g.conv_off + g.conv_region_bytes, g.page_stride)
         assert np.array_equal(a[pad], b[pad])
-        sa = a[g.ssm_off:g.ssm_off + g.ssm_region_bytes].view(np.float32)
-        sb = b[g.ssm_off:g.ssm_off + g.ssm_region_bytes].view(np.float32)
-        fin = np.isfinite(sb)
-        assert np.array_equal(fin, np.isfinite(sa))
-        np.testing.assert_allclose(sa[fin], sb[fin], rtol=0, atol=1e-5 * max(1.0, np.abs(sb[fin]).max()))
+        sa = a[g.ssm_off:g.ssm_off + g.ssm_region_bytes].view(np.uint32)
+        sb = b[g.ssm_off:g.ssm_off + g.ssm_region_bytes].view(np.uint32)
+        assert np.array_equal(sa, sb)

@@ -247,9 +247,9 @@ def bench_restore(steps, warmup):
     ssm = torch.empty((n, g.ssm_region_bytes), dtype=torch.uint8, device="cuda")
     conv = torch.empty((n, g.conv_region_bytes), dtype=torch.uint8, device="cuda")
     layers = [l for l, lin in enumerate(linear) if lin]
-    gather = lambda: [gdn.gdn_gather_states(h, l, idx, n, ssm, conv, stream)  # noqa: E731
+    gather = lambda: [gdn.gdn_gather_states(h, l, idx, n, conv, ssm, stream)  # noqa: E731
                       for l in layers]
-    scatter = lambda: [gdn.gdn_scatter_states(h, l, idx, n, ssm, conv, stream)  # noqa: E731
+    scatter = lambda: [gdn.gdn_scatter_states(h, l, idx, n, conv, ssm, stream)  # noqa: E731
                        for l in layers]
     gs_bytes = 2 * n * len(layers) * payload
     gs = {}

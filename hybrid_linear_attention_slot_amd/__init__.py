@@ -266,18 +266,20 @@ def gdn_restore_slots(pool: Pool, ops, has_initial_state, stream=None) -> int:
                                           _stream(stream)))
 
 
-def gdn_gather_states(pool: Pool, layer: int, idx, n: int, ssm_dense, conv_dense,
+def gdn_gather_states(pool: Pool, layer: int, idx, n: int, conv_dense, ssm_dense,
                       stream=None) -> int:
+    """Dense buffers may be tensors of any element width (their bytes are
+    the bf16 window rows and the fp32 state rows)."""
     return _check(lib().gdn_gather_states(pool.handle, layer, _addr(idx, 4, "idx"), n,
-                                          _addr(ssm_dense, 0, "ssm_dense"),
-                                          _addr(conv_dense, 0, "conv_dense"), _stream(stream)))
+                                          _addr(conv_dense, 0, "conv_dense"),
+                                          _addr(ssm_dense, 0, "ssm_dense"), _stream(stream)))
 
 
-def gdn_scatter_states(pool: Pool, layer: int, idx, n: int, ssm_dense, conv_dense,
+def gdn_scatter_states(pool: Pool, layer: int, idx, n: int, conv_dense, ssm_dense,
                        stream=None) -> int:
     return _check(lib().gdn_scatter_states(pool.handle, layer, _addr(idx, 4, "idx"), n,
-                                           _addr(ssm_dense, 0, "ssm_dense"),
-                                           _addr(conv_dense, 0, "conv_dense"), _stream(stream)))
+                                           _addr(conv_dense, 0, "conv_dense"),
+                                           _addr(ssm_dense, 0, "ssm_dense"), _stream(stream)))
 
 
 def make_step_args(x, conv_w, conv_b, alpha, beta, state_indices, has_initial_state, out,

@@ -260,8 +260,20 @@ int gdn_restore_slots(const gdn_pool* pool, const gdn_restore_op* ops, int32_t n
     return gdn::guarded([&] { return restore(pool, ops, n_ops, hs_dev, stream); });
 }
 
+// The dense buffers: bf16 window rows, fp32 state rows.
+static int check_dense(const gdn_pool* pool, const int32_t* idx, const void* conv_dense,
+                       const void* ssm_dense)
+{
+    if (!idx || (pool->ssm_bytes > 0 && !ssm_dense) || !conv_dense)
+        return fail(GDN_EINVAL, "idx / dense buffers must not be NULL");
+    if ((reinterpret_cast<uintptr_t>(conv_dense) & 1u) != 0 ||
+        (reinterpret_cast<uintptr_t>(ssm_dense) & 3u) != 0)
+        return fail(GDN_EALIGN, "conv_dense must be 2-byte and ssm_dense 4-byte aligned");
+    return GDN_OK;
+}
+
 int gdn_gather_states(const gdn_pool* pool, int32_t layer, const int32_t* idx, int32_t n,
-                      void* ssm_dense, void* conv_dense, gdn_stream_t stream)
+                      void* conv_dense, float* ssm_dense, gdn_stream_t stream)
 {
     gdn::clear_error();
     if (!pool)
@@ -273,14 +285,15 @@ int gdn_gather_states(const gdn_pool* pool, int32_t layer, const int32_t* idx, i
         return fail(GDN_EINVAL, "n < 0");
     if (n == 0)
         return GDN_OK;
-    if (!idx || (pool->ssm_bytes > 0 && !ssm_dense) || !conv_dense)
-        return fail(GDN_EINVAL, "idx / dense buffers must not be NULL");
+    rc = check_dense(pool, idx, conv_dense, ssm_dense);
+    if (rc != GDN_OK)
+        return rc;
     return gdn::launch_gather(pool, layer, idx, n, ssm_dense, conv_dense,
                               reinterpret_cast<hipStream_t>(stream));
 }
 
 int gdn_scatter_states(const gdn_pool* pool, int32_t layer, const int32_t* idx, int32_t n,
-                       const void* ssm_dense, const void* conv_dense, gdn_stream_t stream)
+                       const void* conv_dense, const float* ssm_dense, gdn_stream_t stream)
 {
     gdn::clear_error();
     if (!pool)
@@ -292,8 +305,9 @@ int gdn_scatter_states(const gdn_pool* pool, int32_t layer, const int32_t* idx, 
         return fail(GDN_EINVAL, "n < 0");
     if (n == 0)
         return GDN_OK;
-    if (!idx || (pool->ssm_bytes > 0 && !ssm_dense) || !conv_dense)
-        return fail(GDN_EINVAL, "idx / dense buffers must not be NULL");
+    rc = check_dense(pool, idx, conv_dense, ssm_dense);
+    if (rc != GDN_OK)
+        return rc;
     return gdn::launch_scatter(pool, layer, idx, n, ssm_dense, conv_dense,
                                reinterpret_cast<hipStream_t>(stream));
 }

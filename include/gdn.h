@@ -144,17 +144,20 @@ int gdn_restore_slots(const gdn_pool* pool, const gdn_restore_op* ops_host, int3
 /* ---------------------------------------------------------------------- */
 /* Gather / scatter of indexed rows ("非连续 KV Cache" §4, §5)              */
 /* ---------------------------------------------------------------------- */
-/* gather:  ssm_dense[r] = state payload of page idx[r],
- *          conv_dense[r] = window payload of page idx[r]  (r < n);
+/* gather:  conv_dense[r] = window payload of page idx[r],
+ *          ssm_dense[r]  = state payload of page idx[r]  (r < n);
  *          an out-of-range idx[r] gives zero rows.
  * scatter: the reverse; an out-of-range idx[r] is skipped; padding and
  *          slots not named are left untouched.
- * idx_dev: device int32 [n].  ssm_dense: device [n][ssm_bytes] (may be NULL
- * when ssm_bytes == 0); conv_dense: device [n][conv_bytes].  Bit-exact copies. */
+ * idx_dev: device int32 [n].  conv_dense: device bf16 [n][(W-1) * C]
+ * (2-byte aligned); ssm_dense: device fp32 [n][Hv * dk * dv] (4-byte aligned;
+ * may be NULL for a conv-window-only pool).  Rows are packed back to back in
+ * the dense buffers.  Bit-exact copies.  Errors: GDN_EINVAL (NULL pointer,
+ * n < 0), GDN_ERANGE (layer out of range or attention-only), GDN_EALIGN. */
 int gdn_gather_states(const gdn_pool* pool, int32_t layer, const int32_t* idx_dev, int32_t n,
-                      void* ssm_dense, void* conv_dense, gdn_stream_t stream);
+                      void* conv_dense, float* ssm_dense, gdn_stream_t stream);
 int gdn_scatter_states(const gdn_pool* pool, int32_t layer, const int32_t* idx_dev, int32_t n,
-                       const void* ssm_dense, const void* conv_dense, gdn_stream_t stream);
+                       const void* conv_dense, const float* ssm_dense, gdn_stream_t stream);
 
 /* ---------------------------------------------------------------------- */
 /* Decode step and varlen prefill ("非连续 KV Cache" §5-§6; the Kapitsa     */

@@ -185,6 +185,20 @@ def test_gather_scatter_validation():
         gdn.gdn_scatter_states(p, 0, None, 2, FAKE, FAKE, stream=0)
     assert e.value.code == gdn.GDN_EINVAL
     assert gdn.gdn_gather_states(p, 0, FAKE, 0, FAKE, FAKE, stream=0) == gdn.GDN_OK
+    # argument order (conv_dense, ssm_dense): bf16 rows 2-byte, fp32 rows 4-byte aligned
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.gdn_gather_states(p, 0, FAKE, 2, FAKE + 2, FAKE + 2, stream=0)
+    assert e.value.code == gdn.GDN_EALIGN
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.gdn_scatter_states(p, 0, FAKE, 2, FAKE + 1, FAKE, stream=0)
+    assert e.value.code == gdn.GDN_EALIGN
+    # the state buffer may be NULL only when the pool has no state region
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.gdn_gather_states(p, 0, FAKE, 2, FAKE, None, stream=0)
+    assert e.value.code == gdn.GDN_EINVAL
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.gdn_gather_states(p, 0, FAKE, 2, None, FAKE, stream=0)
+    assert e.value.code == gdn.GDN_EINVAL
 
 
 class _FakeGpuTensor:

@@ -24,14 +24,14 @@ def test_block_stride_example_on_gpu():
     idx = to_dev(np.arange(6, dtype=np.int32))
     dense = torch.zeros((6, 96), dtype=torch.uint8, device="cuda")
     log("gather 48-element blocks")
-    gdn.gdn_gather_states(dp.pool, 0, idx, 6, None, dense)
+    gdn.gdn_gather_states(dp.pool, 0, idx, 6, dense, None)
     torch.cuda.synchronize()
     got = dense.cpu().numpy().view(np.uint16)
     for s in range(6):
         assert np.array_equal(got[s], np.arange(64 * s, 64 * s + 48))
     # scatter into slots 1 and 4, restore 5 -> 2
     src = torch.full((2, 96), 0xFF, dtype=torch.uint8, device="cuda")
-    gdn.gdn_scatter_states(dp.pool, 0, to_dev(np.array([1, 4], np.int32)), 2, None, src)
+    gdn.gdn_scatter_states(dp.pool, 0, to_dev(np.array([1, 4], np.int32)), 2, src, None)
     hs = torch.zeros(1, dtype=torch.uint8, device="cuda")
     assert gdn.gdn_restore_slots(dp.pool, [(2, 5, 1)], hs) == gdn.GDN_OK
     torch.cuda.synchronize()
@@ -121,14 +121,14 @@ def test_gather_scatter_match_oracle(geom):
     sd = torch.full((n, g.ssm_region_bytes), 0x5A, dtype=torch.uint8, device="cuda")
     cd = torch.full((n, g.conv_region_bytes), 0x5A, dtype=torch.uint8, device="cuda")
     log(f"gather/scatter {geom}")
-    gdn.gdn_gather_states(dp.pool, 0, to_dev(idx), n, sd, cd)
+    gdn.gdn_gather_states(dp.pool, 0, to_dev(idx), n, cd, sd)
     torch.cuda.synchronize()
     rs, rc_ = oracle.gather(img, g, idx)
     assert np.array_equal(sd.cpu().numpy(), rs)
     assert np.array_equal(cd.cpu().numpy(), rc_)
     new_s = rng.integers(0, 256, rs.shape, dtype=np.uint8)
     new_c = rng.integers(0, 256, rc_.shape, dtype=np.uint8)
-    gdn.gdn_scatter_states(dp.pool, 0, to_dev(idx), n, to_dev(new_s), to_dev(new_c))
+    gdn.gdn_scatter_states(dp.pool, 0, to_dev(idx), n, to_dev(new_c), to_dev(new_s))
     torch.cuda.synchronize()
     ref = img.copy()
     oracle.scatter(ref, g, idx, new_s, new_c)
@@ -146,12 +146,12 @@ def test_gather_unaligned_dense_rows():
     idx = np.array([5, 1, 2], np.int32)
     cd = torch.zeros((3, g.conv_region_bytes), dtype=torch.uint8, device="cuda")
     assert g.conv_region_bytes % 16 != 0
-    gdn.gdn_gather_states(dp.pool, 0, to_dev(idx), 3, None, cd)
+    gdn.gdn_gather_states(dp.pool, 0, to_dev(idx), 3, cd, None)
     torch.cuda.synchronize()
     _, rc_ = oracle.gather(img, g, idx)
     assert np.array_equal(cd.cpu().numpy(), rc_)
     new_c = rng.integers(0, 256, rc_.shape, dtype=np.uint8)
-    gdn.gdn_scatter_states(dp.pool, 0, to_dev(idx), 3, None, to_dev(new_c))
+    gdn.gdn_scatter_states(dp.pool, 0, to_dev(idx), 3, to_dev(new_c), None)
     torch.cuda.synchronize()
     ref = img.copy()
     oracle.scatter(ref, g, idx, np.zeros((3, 0), np.uint8), new_c)

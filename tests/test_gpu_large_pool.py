@@ -73,9 +73,9 @@ def test_restore_gather_scatter_beyond_4gib(big):
     gidx = high[5:9].astype(np.int32)
     ssm = torch.empty((4, g.ssm_region_bytes), dtype=torch.uint8, device="cuda")
     conv = torch.empty((4, g.conv_region_bytes), dtype=torch.uint8, device="cuda")
-    gdn.gdn_gather_states(dp.pool, 0, to_dev(gidx), 4, ssm, conv)
+    gdn.gdn_gather_states(dp.pool, 0, to_dev(gidx), 4, conv, ssm)
     sidx = np.roll(gidx, 1).astype(np.int32)
-    gdn.gdn_scatter_states(dp.pool, 0, to_dev(sidx), 4, ssm, conv)
+    gdn.gdn_scatter_states(dp.pool, 0, to_dev(sidx), 4, conv, ssm)
     torch.cuda.synchronize()
     ref = img.copy()
     h_ref = hs0.copy()

@@ -113,8 +113,8 @@ def test_window_first_layout_matches_oracle(seed):
     sidx = np.roll(ckpt, 1).astype(np.int32)
     ssm = torch.empty((4, g.ssm_region_bytes), dtype=torch.uint8, device="cuda")
     conv = torch.empty((4, g.conv_region_bytes), dtype=torch.uint8, device="cuda")
-    gdn.gdn_gather_states(dp.pool, 0, to_dev(gidx), 4, ssm, conv)
-    gdn.gdn_scatter_states(dp.pool, 0, to_dev(sidx), 4, ssm, conv)
+    gdn.gdn_gather_states(dp.pool, 0, to_dev(gidx), 4, conv, ssm)
+    gdn.gdn_scatter_states(dp.pool, 0, to_dev(sidx), 4, conv, ssm)
     torch.cuda.synchronize()
     assert np.array_equal(hs.cpu().numpy(), hs_ref)
     od, _ = oracle.gdn_layer(ref, g, dinp.cu_seqlens, live, warm, dinp.x, dinp.conv_w,

@@ -1,0 +1,174 @@
+"""CPU bounds model of the varlen prefill's producer loads (no GPU).
+
+The prefill kernel's producer waves read raw inputs with buffer loads whose
+range check returns zero past a resource's end, so every load either lies
+inside the rows of its own sequence (or its slot's window) or is refused by
+the range check.  A wrong row base or range here once let a wave read past
+the end of x.  This test replays the producers' row / range / offset
+arithmetic for every head size and conv width the kernel is compiled for,
+over ragged lengths, and checks:
+
+  * every load the range check lets through lies inside the sequence's rows
+    of x (token rows [tb, tb + L)), inside one row, on a channel pair the
+    wave owns, and at the row its token needs (so no needed row is refused);
+  * window loads stay inside the window region, and the window resource is
+    empty when the sequence starts cold (a cold page is never read);
+  * gate loads stay inside the sequence's tokens.
+
+The arithmetic is restated from the kernel's `issue` (prefill_kernel.hip);
+a change there must be mirrored here before the kernel runs on a GPU.
+"""
+import numpy as np
+import pytest
+
+CT, NPROD = 16, 4
+INT32_MAX = 2**31 - 1
+OUT_OF_RANGE = 0xFFFFFFF0
+
+
+def shape(dk):
+    kpl = 16 if dk >= 128 else (8 if dk >= 32 else 4)
+    lpc = dk // kpl
+    cpw = 64 // lpc
+    ncons = min(dk // cpw, 4)
+    isz = ncons * cpw
+    tpw = CT // NPROD
+    nvp = isz // 2
+    return dict(ISZ=isz, NSL=dk // isz, TPW=tpw, QKP=dk // 2, NVP=nvp,
+                NVJ=(tpw * nvp + 63) // 64)
+
+
+def range_bytes(n):
+    return min(n, INT32_MAX)
+
+
+def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows):
+    """All producer loads of all workgroups of one sequence."""
+    sh = shape(dk)
+    C = 2 * Hk * dk + Hv * dk
+    rowb = 2 * C
+    HR, TPW = W - 1, sh["TPW"]
+    NR = HR + TPW
+    lane = np.arange(64)
+    nchunks = (L + CT - 1) // CT
+    x_lo, x_hi = tb * rowb, (tb + L) * rowb          # the sequence's bytes of x
+    assert x_hi <= total_rows * rowb
+    n_checked = 0
+    for h in range(Hv):
+        g = h // (Hv // Hk)
+        for sl in range(sh["NSL"]):
+            def chan(ch):
+                ch = np.asarray(ch)
+                return np.where(ch < dk, g * dk + ch,
+                                np.where(ch < 2 * dk, Hk * dk + g * dk + (ch - dk),
+                                         2 * Hk * dk + h * dk + sl * sh["ISZ"] + (ch - 2 * dk)))
+            qkp = np.minimum(lane, sh["QKP"] - 1)
+            oq, ok = chan(2 * qkp) * 2, chan(dk + 2 * qkp) * 2
+            jj = lane[None, :] + 64 * np.arange(sh["NVJ"])[:, None]     # [NVJ, 64]
+            vi, vpj = jj // sh["NVP"], jj % sh["NVP"]
+            cv = chan(2 * dk + 2 * vpj) * 2
+            ov = np.minimum(vi, TPW - 1) * rowb + cv
+            # every owned channel pair lies inside one row of x
+            for off in (oq, ok, cv):
+                assert (off >= 0).all() and (off + 4 <= rowb).all()
+            for pw in range(NPROD):
+                t0 = pw * TPW
+                k = np.arange(nchunks)
+                rbase = k * CT + t0 - HR
+                xb = np.minimum(np.maximum(rbase, 0), L)
+                base = (tb + xb) * rowb                                  # resource base (bytes of x)
+                rng = np.array([range_bytes((L - b) * rowb) for b in xb])
+                # the record count is an unsigned 32-bit field: a negative range
+                # would pass every offset
+                rng = rng % 2**32
+
+                def through(res_base, res_range, off, row_needed):
+                    """Loads at byte offsets `off` of the resource: the ones the
+                    range check lets through must lie in the sequence's rows,
+                    and every needed row must get through."""
+                    off = np.asarray(off, np.int64) % 2**32              # a VGPR offset is unsigned
+                    ok_ = off + 4 <= res_range
+                    addr = res_base + off
+                    assert ((addr >= x_lo) & (addr + 4 <= x_hi))[ok_].all()
+                    need = (row_needed >= 0) & (row_needed < L)
+                    assert (ok_ | ~need).all(), "a row inside the sequence was refused"
+                    return int(ok_.sum())
+
+                main = rbase >= 0
+                for i in range(NR):
+                    row = rbase[:, None] + i                              # token row of load i
+                    for off in (oq, ok):
+                        n_checked += through(base[main, None], rng[main, None],
+                                             (off[None, :] + i * rowb)[np.zeros(main.sum(), int)],
+                                             row[main])
+                for w in range(W):
+                    row = rbase[:, None, None] + np.minimum(vi, TPW - 1)[None] + w
+                    n_checked += through(base[main, None, None], rng[main, None, None],
+                                         np.broadcast_to(ov + w * rowb, (main.sum(),) + ov.shape),
+                                         row[main])
+                if (~main).any():
+                    # the first chunk of wave 0: rows before the start come from the window
+                    assert pw == 0 and rbase[0] == -HR and (~main).sum() == 1
+                    win_range = HR * rowb if warm else 0
+                    for i in range(NR):
+                        r = i - HR
+                        for off in (oq, ok):
+                            if r < 0:
+                                o = (HR + r) * rowb + off
+                                assert ((o >= 0) & (o + 4 <= HR * rowb)).all()
+                                if not warm:
+                                    assert win_range == 0
+                            else:
+                                n_checked += through(base[0], rng[0], r * rowb + off,
+                                                     np.full(64, r))
+                    for w in range(W):
+                        r = np.minimum(vi, TPW - 1) + w - HR
+                        ow = np.where(r < 0, (HR + r) * rowb + cv, OUT_OF_RANGE)
+                        inwin = ow + 4 <= win_range
+                        assert ((ow >= 0) & (ow + 4 <= HR * rowb))[inwin].all()
+                        ox = np.where(r >= 0, r * rowb + cv, OUT_OF_RANGE)
+                        n_checked += through(base[0], rng[0], ox, np.where(r >= 0, r, -1))
+                # gates: token k CT + lane % CT of head h
+                ht = Hv * 4
+                grec = np.array([range_bytes((L - kk * CT) * ht) for kk in k])
+                goff = (lane % CT) * ht
+                okg = goff[None, :] + 4 <= grec[:, None]
+                tok = k[:, None] * CT + (lane % CT)[None, :]
+                assert ((tok >= 0) & (tok < L))[okg].all()
+                assert (okg | (tok >= L)).all()
+    return n_checked
+
+
+C3_LENGTHS = [3561, 2795, 2344, 1479, 1615, 658, 781, 571]
+
+
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_producer_loads_short_and_ragged(dk, W):
+    lengths = list(range(1, 80)) + [1000]
+    Hk, Hv = 1, 2
+    total = sum(lengths)
+    tb = 0
+    n = 0
+    for i, L in enumerate(lengths):
+        n += check_sequence(dk, W, Hk, Hv, L, tb, warm=bool(i % 2), total_rows=total)
+        tb += L
+    assert n > 0
+
+
+@pytest.mark.parametrize("W", [2, 4])
+def test_producer_loads_workload_lengths(W):
+    # the 8-sequence workload's lengths (16 v-heads / 8 k-heads at dk 128),
+    # the last sequence ending exactly at the end of x
+    lengths = C3_LENGTHS
+    total = sum(lengths)
+    tb = 0
+    for i, L in enumerate(lengths):
+        check_sequence(128, W, 2, 4, L, tb, warm=i < 4, total_rows=total)
+        tb += L
+
+
+def test_producer_loads_long_sequence():
+    # one 65,536-token sequence after a 3-token one, at the end of x
+    check_sequence(128, 4, 1, 2, 3, 0, warm=True, total_rows=65539)
+    check_sequence(128, 4, 1, 2, 65536, 3, warm=False, total_rows=65539)

@@ -80,10 +80,13 @@ def test_restore_soft_failure_all_attention():
 
 
 def test_restore_many_ops_and_layers_split_launches():
-    """More ops and layers than one launch carries (kernel-argument budget)."""
+    """More hits and GDN layers than one launch carries (kernel-argument
+    budget: 64 layers, 96 pairs, 96 hs entries): 100 layers of which 75 are
+    GDN layers and ~135 hits, so launches split over both the pairs and the
+    layers (a layer chunk starting at layer 64 of the GDN list)."""
     g = wl.make_geometry(400, Hk=1, Hv=2, dk=16, dv=16, W=4, page_align=128, extra_pad=256)
     rng = wl.rng_for(41)
-    n_layers = 40
+    n_layers = 100
     imgs = [None if l % 4 == 3 else rng.integers(0, 256, (g.num_slots, g.page_stride),
                                                 dtype=np.uint8) for l in range(n_layers)]
     dp = DevicePool(g, imgs)
@@ -95,7 +98,10 @@ def test_restore_many_ops_and_layers_split_launches():
     ops = np.stack([dst, src, req], axis=1).astype(np.int32)
     hs0 = rng.integers(0, 2, n).astype(np.uint8)
     hs = to_dev(hs0)
-    log(f"restore {n} ops x {n_layers} layers")
+    hits = int(((src >= 0) & (req != 0)).sum())
+    n_gdn = sum(im is not None for im in imgs)
+    assert hits > 96 and n_gdn > 64, (hits, n_gdn)
+    log(f"restore {n} ops ({hits} hits) x {n_layers} layers ({n_gdn} GDN)")
     assert gdn.gdn_restore_slots(dp.pool, ops.tolist(), hs) == gdn.GDN_OK
     torch.cuda.synchronize()
     ref = [None if im is None else im.copy() for im in imgs]
@@ -158,45 +164,82 @@ def test_gather_unaligned_dense_rows():
     assert np.array_equal(dp.host(), ref)
 
 
+def _layer_image(g, l):
+    """Layer l's initial pool on the device, regenerated identically on demand:
+    random bytes everywhere, the 4 KiB of padding after each payload included
+    (every page's padding differs from every other's, so a copy that strays
+    into the padding changes bytes)."""
+    gen = torch.Generator(device="cuda").manual_seed(1000 + l)
+    return torch.randint(0, 256, (g.num_slots, g.page_stride), dtype=torch.uint8, device="cuda",
+                         generator=gen)
+
+
 @pytest.mark.slow
-def test_restore_full_hybrid_stack():
+def test_restore_gather_scatter_full_hybrid_stack():
     """64-layer stack (every 4th layer attention-only), 48 GDN layers of 32 heads
-    x 128x128 fp32 + 8192-channel windows, 1024 slots with 4 KiB of non-zero
-    padding per page, 64 ops with a quarter misses.  Pages are checked on the
-    host for a sample of layers against the oracle run on those layers."""
+    x 128x128 fp32 + 8192-channel windows, 1024 slots with 4 KiB of padding
+    per page (random bytes), 64 ops with a quarter misses.  Every GDN layer is checked:
+    the touched pages against the oracle's restore of the layer's initial
+    pages, every other page unchanged.  Then, on every GDN layer, the 64 op rows
+    are gathered to dense rows (against the oracle's gather) and scattered into
+    64 other slots (against the oracle's scatter, padding untouched)."""
     g, linear, ops = wl.restore_workload(seed=0)
     n_layers = len(linear)
-    log(f"allocating {int(linear.sum())} x {g.pool_bytes / 2**30:.1f} GiB")
-    gen = torch.Generator(device="cuda").manual_seed(0)
-    bufs = []
-    for l in range(n_layers):
-        if not linear[l]:
-            bufs.append(None)
-            continue
-        b = torch.randint(0, 256, (g.num_slots, g.page_stride), dtype=torch.uint8,
-                          device="cuda", generator=gen)
-        b[:, g.conv_off + g.conv_region_bytes:] = wl.PAD_BYTE
-        bufs.append(b)
+    gdn_layers = [l for l in range(n_layers) if linear[l]]
+    log(f"allocating {len(gdn_layers)} x {g.pool_bytes / 2**30:.1f} GiB")
+    bufs = [_layer_image(g, l) if linear[l] else None for l in range(n_layers)]
     pool = gdn.gdn_pool_create(bufs, g.num_slots, g.page_stride, g.conv_off, g.ssm_off, g.C,
                                g.W, g.Hk, g.Hv, g.dk, g.dv)
-    sample = [l for l in range(n_layers) if linear[l]][::12] + [n_layers - 2]
-    touched = np.unique(np.concatenate([ops[:, 0], ops[ops[:, 1] >= 0, 1]]))
-    before = {l: bufs[l][torch.from_numpy(touched).cuda()].cpu().numpy() for l in sample}
+    hits = ops[:, 1] >= 0
+    rng = wl.rng_for(5)
+    dsts = ops[:, 0]
+    used = set(dsts.tolist()) | set(ops[hits, 1].tolist())
+    others = np.array([s_ for s_ in rng.permutation(g.num_slots) if s_ not in used][:64], np.int32)
+    touched = np.unique(np.concatenate([dsts, ops[hits, 1], others])).astype(np.int64)
+    remap = {int(s_): i for i, s_ in enumerate(touched)}
+    small = dataclasses.replace(g, num_slots=len(touched))
+    ops_small = np.array([[remap[d], remap[s_] if s_ >= 0 else -1, r] for d, s_, r in ops],
+                         np.int32)
+    t_idx = torch.from_numpy(touched).cuda()
     hs = torch.ones(len(ops), dtype=torch.uint8, device="cuda")
     log("restore 64 ops x 48 layers")
     assert gdn.gdn_restore_slots(pool, ops.tolist(), hs) == gdn.GDN_OK
     torch.cuda.synchronize()
-    h_ref = np.ones(len(ops), np.uint8)
-    remap = {int(s): i for i, s in enumerate(touched)}
-    small = dataclasses.replace(g, num_slots=len(touched))
-    for l in sample:
-        ref = before[l].copy()
-        ops_small = np.array([[remap[d], remap[s] if s >= 0 else -1, r] for d, s, r in ops],
-                             np.int32)
+    h = hs.cpu().numpy()
+    assert h.tolist() == hits.astype(np.uint8).tolist()
+    idx = torch.from_numpy(dsts.astype(np.int32)).cuda()
+    idx2 = torch.from_numpy(others).cuda()
+    n = len(dsts)
+    cd = torch.empty((n, g.conv_region_bytes), dtype=torch.uint8, device="cuda")
+    sd = torch.empty((n, g.ssm_region_bytes), dtype=torch.uint8, device="cuda")
+    rev = torch.arange(n - 1, -1, -1, device="cuda")
+    for l in gdn_layers:
+        init = _layer_image(g, l)
+        changed = torch.nonzero((bufs[l] != init).any(dim=1)).flatten().cpu().numpy()
+        assert set(changed.tolist()) <= set(dsts[hits].tolist()), f"layer {l}: other pages changed"
+        ref = init[t_idx].cpu().numpy()
+        del init
         h = np.ones(len(ops), np.uint8)
-        oracle.restore([ref], small, ops_small, h)
-        h_ref = h
-        got = bufs[l][torch.from_numpy(touched).cuda()].cpu().numpy()
-        assert np.array_equal(got, ref), l
-    assert np.array_equal(hs.cpu().numpy(), h_ref)
-    assert h_ref.sum() == (ops[:, 1] >= 0).sum()
+        assert oracle.restore([ref], small, ops_small, h) == 0
+        assert np.array_equal(h, hs.cpu().numpy())
+        assert np.array_equal(bufs[l][t_idx].cpu().numpy(), ref), f"layer {l}: restore"
+        # gather the 64 op rows
+        cd.fill_(0x5A)
+        sd.fill_(0x5A)
+        gdn.gdn_gather_states(pool, l, idx, n, cd, sd)
+        torch.cuda.synchronize()
+        rs, rc_ = oracle.gather(ref, small, np.array([remap[int(d)] for d in dsts], np.int32))
+        assert np.array_equal(sd.cpu().numpy(), rs), f"layer {l}: gather (state)"
+        assert np.array_equal(cd.cpu().numpy(), rc_), f"layer {l}: gather (window)"
+        # scatter them, in reverse order, into 64 slots no op touches
+        gdn.gdn_scatter_states(pool, l, idx2, n, cd[rev].contiguous(), sd[rev].contiguous())
+        torch.cuda.synchronize()
+        oracle.scatter(ref, small, np.array([remap[int(s_)] for s_ in others], np.int32),
+                       rs[::-1].copy(), rc_[::-1].copy())
+        assert np.array_equal(bufs[l][t_idx].cpu().numpy(), ref), f"layer {l}: scatter"
+        if l % 16 == 0:
+            log(f"layer {l}: restore, gather and scatter match the oracle")
+    log("restore, gather and scatter: all 48 GDN layers match the oracle")
+    gdn.gdn_pool_destroy(pool)
+    del bufs
+    torch.cuda.empty_cache()

@@ -131,6 +131,35 @@ def test_prefill_extreme_decays_match_oracle(d):
     assert np.array_equal(a.host(), b.host()), "split run's pages differ"
 
 
+@pytest.mark.parametrize("d", [32, 128])
+def test_decode_extreme_decays_match_oracle(d):
+    """Decode rows stepped 12 times with decays of 0, 1e-30, a subnormal, runs
+    of 0.02 and exact ones: a = 0 must leave only the rank-one write, a = 1 no
+    decay, and the state must stay finite and within tolerance every step."""
+    g = wl.make_geometry(16, Hk=2, Hv=4, dk=d, dv=d, W=4, page_align=128, extra_pad=128)
+    rows, steps = 6, 12
+    inp, img = case(g, 700 + d, [1] * rows, [1, 0, 1, 1, 0, 1], bias=True)
+    rng = wl.rng_for(701 + d)
+    alphas = extreme_decays(rng, rows * steps, g.Hv).reshape(steps, rows, g.Hv)
+    alphas[0, 0] = 0.0                 # one row forgets everything at its first step
+    alphas[:, 1] = np.float32(1e-40)   # one row decays by a subnormal every step
+    alphas[:, 2] = 1.0                 # one row never decays
+    dp = DevicePool(g, [img])
+    ref = img.copy()
+    log(f"decode extreme decays d={d}: {steps} steps x {rows} rows")
+    for k in range(steps):
+        step = dataclasses.replace(inp, x=wl.draw_x(rng, rows, g.C), alpha=alphas[k].copy(),
+                                   beta=wl.draw_gates(rng, rows, g.Hv)[1],
+                                   has_initial_state=inp.has_initial_state if k == 0 else
+                                   np.ones(rows, np.uint8))
+        t = run_decode(dp, 0, step)
+        torch.cuda.synchronize()
+        o64, _ = oracle_layer(ref, step)
+        check_outputs(u16(t["out"]), o64, f"extreme decays d={d} step {k}")
+    e_st = check_pages(g, dp.host(), ref, slots=inp.state_indices, what=f"extreme decays d={d}")
+    log(f"decode extreme decays d={d}: worst state rel err {e_st:.2e}")
+
+
 def test_prefill_word_aligned_inputs():
     """x only 4-byte and out only 8-byte aligned (views into larger buffers),
     with the last sequence's rows ending exactly at the end of x's buffer and
@@ -212,16 +241,22 @@ def test_padding_rows_and_out_of_range_slots():
     assert (out[:5] == 0).all() and (out[8:] == 0).all()
 
 
-def test_tiny_config_continuation_on_gpu():
+@pytest.mark.parametrize("long_memory", [False, True])
+def test_tiny_config_continuation_on_gpu(long_memory):
     """4 seqs x 64 tokens from a cold start: 64 straight vs 32, restore into the
-    other four slots, 32 more -- bit-exact on the GPU and within tolerance of
-    the oracle; also as 32 decode steps after the restore."""
+    other four slots, 32 more -- as a prefill and as decode steps, each
+    bit-exact against its own straight run on the GPU and within tolerance of
+    the oracle.  With the long-memory gate alpha = exp(-0.01 softplus(z)) the
+    state after the restore point still carries the first 32 tokens, so a
+    continuation from a cold slot must differ (the check is sensitive)."""
     g = wl.tiny_geometry(extra_pad=128)
     rng = wl.rng_for(0)
     perm = rng.permutation(g.num_slots).astype(np.int32)
     A, B = perm[:4], perm[4:]
     img = wl.make_pool_image(g, rng, warm_slots=[], nan_slots=A)
-    full = wl.step_inputs(g, rng, [64] * 4, A, np.zeros(4, np.uint8), bias=True)
+    full = wl.step_inputs(g, rng, [64] * 4, A, np.zeros(4, np.uint8), bias=True,
+                          long_memory=long_memory)
+    what = "tiny long-memory" if long_memory else "tiny"
 
     def part(t0, t1, slots, hs):
         sel = np.concatenate([np.arange(i * 64 + t0, i * 64 + t1) for i in range(4)])
@@ -230,38 +265,75 @@ def test_tiny_config_continuation_on_gpu():
                                    has_initial_state=np.asarray(hs, np.uint8),
                                    cu_seqlens=np.arange(5, dtype=np.int32) * (t1 - t0))
 
+    def restore(dp, hs_val=1):
+        hs = torch.full((4,), hs_val, dtype=torch.uint8, device="cuda")
+        assert gdn.gdn_restore_slots(dp.pool, [(int(b), int(a), 1) for a, b in zip(A, B)],
+                                     hs) == gdn.GDN_OK
+        return hs
+
+    def decode_steps(dp, t0, t1, slots, hs0):
+        outs = []
+        for t in range(t0, t1):
+            hs = hs0 if t == t0 else [1] * 4
+            outs.append(u16(run_decode(dp, 0, part(t, t + 1, slots, hs))["out"]))
+        return np.stack(outs, axis=1)  # [4, steps, Hv, dv]
+
+    def payload(host, s_):
+        return host[s_][:g.conv_off + g.conv_region_bytes]
+
+    log(f"{what}: prefill straight vs 32 + restore + 32")
     straight = DevicePool(g, [img])
     t_s = run_prefill(straight, 0, full)
     split = DevicePool(g, [img])
     run_prefill(split, 0, part(0, 32, A, [0] * 4))
-    hs = torch.ones(4, dtype=torch.uint8, device="cuda")
-    assert gdn.gdn_restore_slots(split.pool, [(int(b), int(a), 1) for a, b in zip(A, B)],
-                                 hs) == gdn.GDN_OK
+    restore(split)
     t_2 = run_prefill(split, 0, part(32, 64, B, [1] * 4))
-    # the same continuation as 32 decode steps
+    # the same continuation as 32 decode steps after the restore
     dec = DevicePool(g, [img])
     run_prefill(dec, 0, part(0, 32, A, [0] * 4))
-    gdn.gdn_restore_slots(dec.pool, [(int(b), int(a), 1) for a, b in zip(A, B)], hs)
-    dec_out = []
-    for t in range(32, 64):
-        dec_out.append(u16(run_decode(dec, 0, part(t, t + 1, B, [1] * 4))["out"]))
+    restore(dec)
+    d_cont = decode_steps(dec, 32, 64, B, [1] * 4)
+    # decode all the way: 64 steps straight vs 32 + restore + 32
+    log(f"{what}: decode straight vs 32 + restore + 32")
+    d_straight_pool = DevicePool(g, [img])
+    d_straight = decode_steps(d_straight_pool, 0, 64, A, [0] * 4)
+    d_split_pool = DevicePool(g, [img])
+    decode_steps(d_split_pool, 0, 32, A, [0] * 4)
+    restore(d_split_pool)
+    d_split = decode_steps(d_split_pool, 32, 64, B, [1] * 4)
     torch.cuda.synchronize()
     o_s = u16(t_s["out"]).reshape(4, 64, g.Hv, g.dv)
     o_2 = u16(t_2["out"]).reshape(4, 32, g.Hv, g.dv)
-    assert np.array_equal(o_2, o_s[:, 32:]), "restored continuation differs from straight run"
+    assert np.array_equal(o_2, o_s[:, 32:]), "restored prefill differs from the straight run"
+    assert np.array_equal(d_split, d_straight[:, 32:]), "restored decode differs from straight"
     host_s, host_2 = straight.host(), split.host()
+    host_ds, host_d2 = d_straight_pool.host(), d_split_pool.host()
     for a, b in zip(A, B):
-        assert np.array_equal(host_2[b][:g.conv_off + g.conv_region_bytes],
-                              host_s[a][:g.conv_off + g.conv_region_bytes])
+        assert np.array_equal(payload(host_2, b), payload(host_s, a))
+        assert np.array_equal(payload(host_d2, b), payload(host_ds, a))
     # against the oracle
     ref = img.copy()
     o64, _ = oracle_layer(ref, full)
-    check_outputs(u16(t_s["out"]), o64, "tiny straight")
-    check_pages(g, host_s, ref, slots=A, what="tiny straight")
+    check_outputs(u16(t_s["out"]), o64, f"{what} straight prefill")
+    check_pages(g, host_s, ref, slots=A, what=f"{what} straight prefill")
+    check_pages(g, host_ds, ref, slots=A, what=f"{what} straight decode")
     o64 = o64.reshape(4, 64, g.Hv, g.dv)
-    d = np.stack(dec_out, axis=1)  # [4, 32, Hv, dv]
-    check_outputs(d.reshape(-1, g.Hv, g.dv), o64[:, 32:].reshape(-1, g.Hv, g.dv),
-                  "tiny decode continuation")
+    check_outputs(d_straight.reshape(-1, g.Hv, g.dv), o64.reshape(-1, g.Hv, g.dv),
+                  f"{what} straight decode")
+    check_outputs(d_cont.reshape(-1, g.Hv, g.dv), o64[:, 32:].reshape(-1, g.Hv, g.dv),
+                  f"{what} decode continuation")
+    if long_memory:
+        # a continuation that starts cold (a lost restore) is outside the tolerance
+        cold = DevicePool(g, [img])
+        run_prefill(cold, 0, part(0, 32, A, [0] * 4))
+        t_c = run_prefill(cold, 0, part(32, 64, B, [0] * 4))
+        torch.cuda.synchronize()
+        with pytest.raises(AssertionError):
+            check_outputs(u16(t_c["out"]), o64[:, 32:].reshape(-1, g.Hv, g.dv), "cold")
+        oc = wl.bf16_bits_to_f32(u16(t_c["out"]).reshape(4, 32, g.Hv, g.dv)).astype(np.float64)
+        ref_last = o64[:, -1]
+        rel = np.abs(oc[:, -1] - ref_last).max(-1) / np.abs(ref_last).max(-1)
+        assert (rel > 0.05).all(), "the long-memory state forgot the restored part"
 
 
 @pytest.mark.parametrize("extra_pad", [0, 4096])

@@ -9,13 +9,20 @@
 // the end of a payload and the next page is skipped by stride, never read or
 // written ("非连续 KV Cache" §3.2-§3.4).
 //
-// The copies are HBM-bound.  Each workgroup of 1024 threads moves one 128 KiB
-// chunk of one region: every lane issues eight 16-byte loads before its eight
-// stores, so a wave keeps 8 KiB in flight and every load instruction of the
-// workgroup reads 16 KiB of consecutive bytes (on the 48-layer restore this
-// ran 10 % faster than 256-thread workgroups moving 32 KiB).  Regions whose
-// bytes are not a multiple of 16 finish with 2-byte element copies.
+// The copies are HBM-bound.  Each workgroup of 1024 threads moves 128 KiB at
+// a time: every lane issues eight 16-byte loads before its eight stores, so a
+// wave keeps 8 KiB in flight and every load instruction of the workgroup reads
+// 16 KiB of consecutive bytes (on the 48-layer restore this ran 10 % faster
+// than 256-thread workgroups moving 32 KiB).  The restore launches one
+// workgroup per 128 KiB chunk of each (pair, layer, region): tens of thousands
+// of them, so the last partial round of the GPU's resident workgroups is a
+// small share.  A gather or scatter call moves only one layer's rows (about a
+// thousand chunks), so there every resident workgroup takes an equal
+// contiguous share of the call's 16-byte units instead and all of them finish
+// together.  Regions whose bytes are not a multiple of 16 (or dense rows not
+// 16-byte aligned) use 2-byte element copies.
 #include <algorithm>
+#include <atomic>
 
 #include "device_utils.h"
 #include "gdn_internal.h"
@@ -177,6 +184,131 @@ __global__ __launch_bounds__(kCopyThreads) void rows_kernel(RowCopyArgs a)
         copy_region_chunk(page, dense, bytes, chunk, a.vec[reg] != 0);
 }
 
+// Copy n consecutive 16-byte units (n < 2^27) through buffer resources of
+// exactly n units: whole 128 KiB blocks with eight loads in flight per lane
+// ahead of the stores, then the remainder over as many rounds of 1024 units as
+// it needs (uniform); the range check returns zero for loads and drops stores
+// past the end, so the last round needs no guard.  Loads take the block offset
+// in an SGPR; stores take their whole offset in the VGPR (a 128-bit store with
+// an SGPR offset can read its data registers after a later write to them).
+constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer resource, gfx9-family layout
+constexpr int kNonTemporal = 2;          // cache-policy bit: streamed once
+constexpr int64_t kMaxPieceUnits = int64_t(1) << 27; // 2 GiB per buffer resource
+
+// A wave-uniform value the compiler computed in vector registers (64-bit
+// division is vector code) moved to scalar registers, so that buffer resources
+// built from it need no loop over distinct values.
+__device__ __forceinline__ int64_t uniform64(int64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
+    return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ void copy_units(uint8_t* dst, const uint8_t* src, int64_t n)
+{
+    constexpr int kBlockUnits = kCopyThreads * kCopyUnroll;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(src), short(0), int(n * 16), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rd =
+        __builtin_amdgcn_make_buffer_rsrc(dst, short(0), int(n * 16), kBufferWord3);
+    const int lane = int(threadIdx.x) * 16;
+    const int ni = int(n);
+    int i = 0;
+    for (; i + kBlockUnits <= ni; i += kBlockUnits) {
+        u32x4 v[kCopyUnroll];
+#pragma unroll
+        for (int k = 0; k < kCopyUnroll; ++k)
+            v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane, (i + k * kCopyThreads) * 16,
+                                                         kNonTemporal);
+#pragma unroll
+        for (int k = 0; k < kCopyUnroll; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(v[k], rd, lane + (i + k * kCopyThreads) * 16,
+                                                   0, kNonTemporal);
+    }
+    const int rounds = (ni - i + kCopyThreads - 1) / kCopyThreads; // 0..7, uniform
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int k = 0; k < kCopyUnroll; ++k)
+        if (k < rounds)
+            v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane, (i + k * kCopyThreads) * 16,
+                                                         kNonTemporal);
+#pragma unroll
+    for (int k = 0; k < kCopyUnroll; ++k)
+        if (k < rounds)
+            __builtin_amdgcn_raw_buffer_store_b128(v[k], rd, lane + (i + k * kCopyThreads) * 16,
+                                                   0, kNonTemporal);
+}
+
+__device__ __forceinline__ void zero_units(uint8_t* dst, int64_t n)
+{
+    const __amdgpu_buffer_rsrc_t rd =
+        __builtin_amdgcn_make_buffer_rsrc(dst, short(0), int(n * 16), kBufferWord3);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int j = int(threadIdx.x); j < int(n); j += kCopyThreads)
+        __builtin_amdgcn_raw_buffer_store_b128(z, rd, j * 16, 0, kNonTemporal);
+}
+
+// Gather / scatter with 16-byte aligned regions and dense rows.  The call's
+// units are numbered row by row (row r: its state units, then its window
+// units); workgroup w of the grid takes units [U w / G, U (w + 1) / G) and
+// walks the (row, region) pieces they cover.  All indices are wave-uniform.
+template <bool kGather>
+__global__ __launch_bounds__(kCopyThreads) void rows_balanced_kernel(RowCopyArgs a)
+{
+    const int64_t us = a.r.bytes[0] >> 4, uw = a.r.bytes[1] >> 4;
+    const int64_t upr = us + uw; // units per row
+    const int64_t total = upr * a.n;
+    const int64_t end = total * (blockIdx.x + 1) / gridDim.x;
+    int64_t u = total * blockIdx.x / gridDim.x;
+    while (u < end) {
+        const int64_t row = u / upr;
+        const int64_t ur = u - row * upr;
+        const int reg = ur < us ? 0 : 1;
+        const int64_t off = reg == 0 ? ur : ur - us;         // units into the region
+        const int64_t len =
+            uniform64(min(min(end - u, (reg == 0 ? us : uw) - off), kMaxPieceUnits));
+        uint8_t* dense = reinterpret_cast<uint8_t*>(uniform64(
+            reinterpret_cast<int64_t>(a.dense[reg] + row * a.r.bytes[reg] + off * 16)));
+        const int32_t slot = __builtin_amdgcn_readfirstlane(a.idx[uniform64(row)]);
+        if (slot >= 0 && slot < a.num_slots) {
+            uint8_t* page = reinterpret_cast<uint8_t*>(uniform64(reinterpret_cast<int64_t>(
+                a.base + int64_t(slot) * a.page_stride + a.r.off[reg] + off * 16)));
+            if (kGather)
+                copy_units(dense, page, len);
+            else
+                copy_units(page, dense, len);
+        } else if (kGather) {
+            zero_units(dense, len);
+        }
+        u += len;
+    }
+}
+
+// Workgroups of `kernel` the device can hold at once (CUs x occupancy),
+// looked up once per device.
+int resident_copy_workgroups(const void* kernel)
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kCopyThreads, 0) !=
+            hipSuccess)
+        return 0;
+    const int r = std::max(1, cus) * std::max(1, per_cu);
+    if (dev < 64)
+        cache[dev].store(r, std::memory_order_relaxed);
+    return r;
+}
+
 Regions regions_of(const gdn_pool* pool)
 {
     Regions r;
@@ -209,6 +341,26 @@ int launch_rows(bool gather, const gdn_pool* pool, int32_t layer, const int32_t*
     const int64_t blocks = per_row * n;
     if (blocks == 0)
         return GDN_OK;
+    if (a.vec[0] && a.vec[1]) {
+        // balanced: at most one resident round of workgroups, none with less
+        // than one 128 KiB block of work
+        const void* k = gather ? reinterpret_cast<const void*>(&rows_balanced_kernel<true>)
+                               : reinterpret_cast<const void*>(&rows_balanced_kernel<false>);
+        const int resident = resident_copy_workgroups(k);
+        if (resident <= 0)
+            return fail(GDN_EHIP, "cannot query the device's workgroup capacity");
+        const int64_t units = (a.r.bytes[0] + a.r.bytes[1]) / 16 * n;
+        const int64_t per_block = int64_t(kCopyThreads) * kCopyUnroll;
+        const int64_t grid = std::max<int64_t>(
+            1, std::min<int64_t>(resident, (units + per_block - 1) / per_block));
+        if (gather)
+            hipLaunchKernelGGL(rows_balanced_kernel<true>, dim3(uint32_t(grid)),
+                               dim3(kCopyThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL(rows_balanced_kernel<false>, dim3(uint32_t(grid)),
+                               dim3(kCopyThreads), 0, stream, a);
+        return check_launch(gather ? "gather" : "scatter");
+    }
     if (blocks > INT32_MAX)
         return fail(GDN_ERANGE, "too many rows for one launch");
     if (gather)

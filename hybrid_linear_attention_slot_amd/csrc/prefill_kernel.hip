@@ -353,6 +353,8 @@ void prefill_kernel(PrefillParams p)
                           int64_t(h) * DK * DV;
             }
         }
+        // the chunk holding the checkpoint token (-1: none; -1 / CT would be 0)
+        const int ck_chunk = ck_tok >= 0 ? ck_tok / CT : -1;
         const __amdgpu_buffer_rsrc_t ck_rs = __builtin_amdgcn_make_buffer_rsrc(
             ck_tile, short(0), ck_tok >= 0 ? DK * DV * 4 : 0, 0x00020000);
         const int voff = (4 * jl * DV + gcol) * 4;
@@ -388,7 +390,7 @@ void prefill_kernel(PrefillParams p)
                         store_ck();
                 }
             };
-            if (nt == CT && ck_tok / CT != c && quiet) {
+            if (nt == CT && ck_chunk != c && quiet) {
                 // full chunk: a fully unrolled loop without branches (every LDS
                 // address is a base plus an immediate), in which the operands of
                 // token t+1 are requested before token t is computed; the

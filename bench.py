@@ -344,6 +344,56 @@ def bench_copy(reps=10):
                     f"{reps} per-call events"}
 
 
+def bench_ceilings(reps=10):
+    """HBM ceilings on this GPU for the path's access patterns (the kernels of
+    libgdn_ceilings.so: no arithmetic, only the bytes): a 2 GiB read-only
+    stream, a 2 GiB write-only stream, and the decode's pattern, an in-place
+    read-modify-write of the 2 MiB state region of 256 scattered pages of a
+    1024-page pool with the decode's page stride.  Median of per-call events."""
+    import ctypes
+
+    import torch
+    import workloads as wl
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "hybrid_linear_attention_slot_amd",
+                                   "libgdn_ceilings.so"))
+    p, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+    lib.gdnc_read.argtypes = [p, i64, p, p]
+    lib.gdnc_write.argtypes = [p, i64, u32, p]
+    lib.gdnc_rmw.argtypes = [p, i64, p, i32, i64, p]
+    st = torch.cuda.current_stream()
+    sp = st.cuda_stream
+    n = 2 << 30
+    buf = torch.ones(n, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(n // (128 << 10), dtype=torch.int32, device="cuda")
+
+    def run(fn):
+        for _ in range(2):
+            assert fn() == 0
+        return per_call(lambda: fn(), reps, st)["p50"]
+
+    rd = run(lambda: lib.gdnc_read(buf.data_ptr(), n, sink.data_ptr(), sp))
+    wr = run(lambda: lib.gdnc_write(buf.data_ptr(), n, 7, sp))
+    del buf, sink
+    inp, _ = wl.decode_workload(seed=0)
+    g = inp.geom
+    assert g.ssm_off == 0 and g.ssm_region_bytes == 2 << 20
+    pool = torch.ones((g.num_slots, g.page_stride), dtype=torch.uint8, device="cuda")
+    pages = dev(inp.state_indices)
+    nb = 2 * inp.num_seqs * g.ssm_region_bytes
+    rmw = run(lambda: lib.gdnc_rmw(pool.data_ptr(), g.page_stride, pages.data_ptr(),
+                                   inp.num_seqs, g.ssm_region_bytes, sp))
+    del pool
+    torch.cuda.empty_cache()
+    return {"read_gb_per_s": round(n / (rd * 1e-3) / 1e9, 1),
+            "write_gb_per_s": round(n / (wr * 1e-3) / 1e9, 1),
+            "rmw_gb_per_s": round(nb / (rmw * 1e-3) / 1e9, 1),
+            "what": "libgdn_ceilings kernels: 2 GiB read-only and write-only streams, and the "
+                    "in-place read-modify-write of the 2 MiB state region of the decode "
+                    "workload's 256 pages (read + write bytes); 1024-thread workgroups, 128 KiB "
+                    f"each, non-temporal; median of {reps} per-call events"}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -391,6 +441,88 @@ def cpu_baseline(inp_decode, min_seconds=10.0, single_thread_seconds=4.0):
             "single_thread_sample": f"{reps1} repetitions on 1 thread, {dt1:.1f} s"}
 
 
+def cpu_baseline_prefill(threads=None, single_thread_seqs=4):
+    """The oracle on the 8-sequence prefill workload: the whole workload once
+    with OpenMP over sequences (8 sequences, so at most 8 threads work), then
+    the shortest `single_thread_seqs` sequences on one thread; tokens/s."""
+    import dataclasses
+
+    import oracle
+    import workloads as wl
+
+    inp, img = wl.prefill_workload(seed=0)
+    g = inp.geom
+    threads = threads or min(os.cpu_count() or 1, 16)
+
+    def run(sub, n_threads):
+        oracle.set_threads(n_threads)
+        work = img.copy()
+        t0 = time.perf_counter()
+        oracle.gdn_layer(work, g, sub.cu_seqlens, sub.state_indices, sub.has_initial_state,
+                         sub.x, sub.conv_w, sub.conv_b, sub.alpha, sub.beta)
+        return time.perf_counter() - t0, oracle.get_threads()
+
+    dt, got = run(inp, threads)
+    lens = np.diff(inp.cu_seqlens)
+    pick = np.sort(np.argsort(lens, kind="stable")[:single_thread_seqs])
+    rows = np.concatenate([np.arange(inp.cu_seqlens[i], inp.cu_seqlens[i + 1]) for i in pick])
+    cu = np.zeros(len(pick) + 1, np.int32)
+    cu[1:] = np.cumsum(lens[pick])
+    sub = dataclasses.replace(inp, x=inp.x[rows], alpha=inp.alpha[rows], beta=inp.beta[rows],
+                              cu_seqlens=cu, state_indices=inp.state_indices[pick],
+                              has_initial_state=inp.has_initial_state[pick])
+    dt1, _ = run(sub, 1)
+    return {"value": round(inp.total_tokens / dt, 1), "unit": "tokens/s",
+            "cores": min(got, inp.num_seqs), "kind": "oracle", "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count(),
+            "sample": f"the whole 8-sequence prefill ({inp.total_tokens} tokens, 16 heads) once, "
+                      f"{dt:.1f} s, fp64 C oracle with OpenMP over sequences ({got} threads "
+                      f"offered, one per sequence busy)",
+            "single_thread_value": round(sub.total_tokens / dt1, 1),
+            "single_thread_sample": f"the {len(pick)} shortest sequences ({sub.total_tokens} "
+                                    f"tokens) on 1 thread, {dt1:.1f} s"}
+
+
+def cpu_baseline_restore(n_layers=11):
+    """The oracle's restore of the 48-layer workload's 64 ops on a bounded
+    sample of the stack: its first `n_layers` layers (9 GDN layers, every 4th
+    attention-only), each a distinct host image of the touched pages, so that
+    every page copy streams from memory; GB/s of the algorithmic bytes of the
+    sample (the same bytes per GDN layer as the GPU restore)."""
+    import dataclasses
+
+    import oracle
+    import workloads as wl
+
+    g, linear, ops = wl.restore_workload(seed=0)
+    linear = linear[:n_layers]
+    hits = ops[:, 1] >= 0
+    touched = np.unique(np.concatenate([ops[:, 0], ops[hits, 1]]))
+    remap = {int(s_): i for i, s_ in enumerate(touched)}
+    small = dataclasses.replace(g, num_slots=len(touched))
+    ops_small = np.array([[remap[int(d)], remap[int(s_)] if s_ >= 0 else -1, r]
+                          for d, s_, r in ops], np.int32)
+    rng = np.random.default_rng(0)
+    layers = [rng.integers(0, 256, (small.num_slots, g.page_stride), dtype=np.uint8)
+              if lin else None for lin in linear]
+    hs = np.ones(len(ops), np.uint8)
+    oracle.restore(layers, small, ops_small, hs)  # first touch of the pages
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.restore(layers, small, ops_small, hs)
+        reps += 1
+        if time.perf_counter() - t0 >= 3.0:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = 2 * int(hits.sum()) * int(linear.sum()) * (g.ssm_region_bytes + g.conv_region_bytes)
+    return {"value": round(nbytes * reps / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"the restore of the 64 ops ({int(hits.sum())} hits) over the stack's "
+                      f"first {len(linear)} layers ({int(linear.sum())} GDN layers, distinct "
+                      f"host images of the touched pages), {reps} repetitions, {dt:.1f} s, "
+                      "plain C memcpy per (op, layer) region on one thread"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,6 +533,9 @@ def main():
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (3 times), the known-size "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--only", choices=["prefill", "prefill32", "ceilings"],
+                    help="run one secondary leg alone and print its figures (for counter "
+                         "passes under rocprofv3); no bench line")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU only: the slot-state path has no cross-GPU step "
@@ -420,6 +555,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
+    if a.only:
+        if a.only == "prefill":
+            pinp, ppc, _ = bench_prefill(a.steps, a.warmup)
+            part = {"prefill_ms_p50": round(ppc["p50"], 4), "tokens": pinp.total_tokens}
+        elif a.only == "prefill32":
+            part = bench_prefill_32heads(a.steps, a.warmup)
+        else:
+            part = bench_ceilings()
+        print(json.dumps({"only": a.only, **part}), flush=True)
+        return
     inp, ms, nbytes, dpc = bench_decode(a.steps, a.warmup)
     gbs = nbytes / (ms * 1e-3) / 1e9
     _, ms_pad, nbytes_pad, _ = bench_decode(a.steps, a.warmup, extra_pad=4096)
@@ -482,9 +627,15 @@ def main():
         "restore": restore,
     }
     line["copy_baseline"] = bench_copy()
+    ceil = bench_ceilings()
+    ceil["decode_frac_of_rmw"] = round(gbs / ceil["rmw_gb_per_s"], 4)
+    line["hbm_ceilings"] = ceil
     line["slot_manager"] = bench_slot_manager()
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
+        prefill["cpu_baseline"] = cpu_baseline_prefill()
+        if restore is not None:
+            restore["cpu_baseline"] = cpu_baseline_restore()
     print(json.dumps(line), flush=True)
 
 

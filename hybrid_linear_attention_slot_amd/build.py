@@ -20,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libgdn.so")
+CEILINGS_SRC = os.path.join(PKG, "ceilings", "hbm_ceilings.hip")
+CEILINGS_LIB = os.path.join(PKG, "libgdn_ceilings.so")
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 
@@ -67,7 +69,23 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB_PATH)
     if verbose:
         print("built", LIB_PATH)
+    build_ceilings(verbose)
     return LIB_PATH
+
+
+def build_ceilings(verbose: bool = False) -> str:
+    """The HBM-ceiling kernels the benchmark sets the path's kernels against
+    (a separate library: not part of the state library's ABI)."""
+    obj = _compile(CEILINGS_SRC)
+    tmp = CEILINGS_LIB + ".tmp"
+    r = subprocess.run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, CEILINGS_LIB)
+    if verbose:
+        print("built", CEILINGS_LIB)
+    return CEILINGS_LIB
 
 
 if __name__ == "__main__":

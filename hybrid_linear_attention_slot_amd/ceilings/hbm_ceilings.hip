@@ -1,0 +1,124 @@
+// HBM ceilings of MI355X for the access patterns of the state path (gfx950).
+//
+// Measurement aids, not part of the state library: three kernels that move
+// bytes the way the path's kernels do, with no arithmetic, so that a kernel's
+// bandwidth can be set against what its access pattern reaches on the same
+// GPU:
+//   read  -- stream a buffer in, 128 KiB per 1024-thread workgroup, eight
+//            16-byte non-temporal loads in flight per lane;
+//   write -- stream a buffer out the same way;
+//   rmw   -- in place read-modify-write of the state regions of scattered
+//            pages (the decode step's pattern: each row's 2 MiB of state is
+//            read and written back in its own page), one workgroup per 128 KiB
+//            of a region, all eight loads of a lane before its stores.
+// Built as its own library (libgdn_ceilings.so); the benchmark calls it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 1024;
+constexpr int kUnroll = 8;
+constexpr int64_t kChunkUnits = int64_t(kThreads) * kUnroll; // 16-byte units per workgroup
+constexpr int64_t kChunkBytes = kChunkUnits * 16;            // 128 KiB
+
+__global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ src,
+                                                        uint32_t* __restrict__ sink)
+{
+    const int64_t u0 = int64_t(blockIdx.x) * kChunkUnits + threadIdx.x;
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k)
+        v[k] = __builtin_nontemporal_load(&src[u0 + int64_t(k) * kThreads]);
+    uint32_t x = 0;
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k)
+        x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    // a store that depends on the data keeps the loads live; it almost never
+    // happens, so the kernel's traffic is the read alone
+    if (x == 0x9E3779B9u)
+        sink[blockIdx.x] = x;
+}
+
+__global__ __launch_bounds__(kThreads) void write_kernel(u32x4* __restrict__ dst, uint32_t value)
+{
+    const int64_t u0 = int64_t(blockIdx.x) * kChunkUnits + threadIdx.x;
+    const u32x4 v = {value, value ^ 1u, value ^ 2u, value ^ 3u};
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k)
+        __builtin_nontemporal_store(v, &dst[u0 + int64_t(k) * kThreads]);
+}
+
+// Workgroup b: chunk b % chunks_per_page of the region of page pages[b / chunks_per_page].
+__global__ __launch_bounds__(kThreads) void rmw_kernel(uint8_t* __restrict__ base,
+                                                       int64_t page_stride,
+                                                       const int32_t* __restrict__ pages,
+                                                       int32_t chunks_per_page, uint32_t mask)
+{
+    const int p = blockIdx.x / chunks_per_page;
+    const int c = blockIdx.x - p * chunks_per_page;
+    u32x4* r = reinterpret_cast<u32x4*>(base + int64_t(pages[p]) * page_stride) +
+               int64_t(c) * kChunkUnits + threadIdx.x;
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k)
+        v[k] = __builtin_nontemporal_load(&r[int64_t(k) * kThreads]);
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+        // every word changes by a mask only known at run time, so the compiler
+        // can neither drop the store nor narrow it to the changed bytes
+        v[k] ^= mask;
+        __builtin_nontemporal_store(v[k], &r[int64_t(k) * kThreads]);
+    }
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? 0 : -1; }
+
+} // namespace
+
+extern "C" {
+
+// Reads `bytes` (a positive multiple of 128 KiB, 16-byte aligned) of `src`;
+// `sink` holds bytes / 128 KiB words (rarely written).  0 on success, -1 on a
+// bad argument or a refused launch.
+int gdnc_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream)
+{
+    if (!src || !sink || bytes <= 0 || bytes % kChunkBytes != 0 || bytes / kChunkBytes > INT32_MAX)
+        return -1;
+    hipLaunchKernelGGL(read_kernel, dim3(uint32_t(bytes / kChunkBytes)), dim3(kThreads), 0, stream,
+                       static_cast<const u32x4*>(src), sink);
+    return launched();
+}
+
+// Writes `bytes` (a positive multiple of 128 KiB) of `dst`.
+int gdnc_write(void* dst, int64_t bytes, uint32_t value, hipStream_t stream)
+{
+    if (!dst || bytes <= 0 || bytes % kChunkBytes != 0 || bytes / kChunkBytes > INT32_MAX)
+        return -1;
+    hipLaunchKernelGGL(write_kernel, dim3(uint32_t(bytes / kChunkBytes)), dim3(kThreads), 0,
+                       stream, static_cast<u32x4*>(dst), value);
+    return launched();
+}
+
+// Read-modify-write in place of the first `region_bytes` (a positive multiple
+// of 128 KiB) of each page pages_dev[i], i < n_pages, at base + page *
+// page_stride (16-byte aligned).  The pages must be distinct and inside the
+// caller's buffer (not checkable here).
+int gdnc_rmw(void* base, int64_t page_stride, const int32_t* pages_dev, int32_t n_pages,
+             int64_t region_bytes, hipStream_t stream)
+{
+    if (!base || !pages_dev || n_pages <= 0 || region_bytes <= 0 ||
+        region_bytes % kChunkBytes != 0 || page_stride < region_bytes || page_stride % 16 != 0)
+        return -1;
+    const int64_t per_page = region_bytes / kChunkBytes;
+    if (per_page * n_pages > INT32_MAX)
+        return -1;
+    hipLaunchKernelGGL(rmw_kernel, dim3(uint32_t(per_page * n_pages)), dim3(kThreads), 0, stream,
+                       static_cast<uint8_t*>(base), page_stride, pages_dev, int32_t(per_page),
+                       0x01010101u);
+    return launched();
+}
+
+} // extern "C"

@@ -4,47 +4,69 @@
 // Sequence n covers tokens [cu[n], cu[n+1]) and owns slot state_indices[n].
 // Its window and state are gathered once (or taken as zero when
 // has_initial_state is 0, "Linear-State Prefix Cache 内部机制" §4.1), the
-// causal conv + SiLU, the q/k L2 norms and the gated delta rule run token by
-// token with the state kept on chip ("Kapitsa 源码拆解 05": the work per
+// causal conv + SiLU, the q/k L2 norms and the gated delta rule run over the
+// sequence with the state kept on chip ("Kapitsa 源码拆解 05": the work per
 // token does not grow with the history), and the final window and state are
 // scattered back into the same page ("非连续 KV Cache" §5-§6).
 //
-// Parallel structure.  Every value column of a head's state evolves on its
-// own once k, v, a, b of the token are known, so a workgroup takes one
-// (sequence, v-head, slice of ISZ value columns) and keeps that slice of the
-// state in registers for the whole sequence.  Its waves have two roles:
-//   - consumer waves run the recurrence and nothing else.  A lane holds KPL
-//     keys of one value column (keys 4 jl + 4 LPC m + e, so that the LPC
-//     lanes of a column read one contiguous run of k from LDS); S k is a
-//     lane-partial dot product finished with DPP sums over the LPC lanes,
-//     d = b (v - a S_old k^) and S <- a S_old + d k^T.  A consumer writes d of
-//     every token, and the state at the start of every chunk, to LDS;
-//   - producer waves prepare the next chunk of CT tokens while the consumers
-//     work on the current one (raw inputs loaded into registers a chunk
-//     ahead, conv + SiLU, norm factors, decay products), and form the
-//     outputs of a chunk from what the consumers left, on the matrix cores.
-//     Within a chunk, with S_0 the state at its start, A_t the product of the
-//     chunk's decays through token t and D the chunk's d values,
-//         o_t = S_t q^_t = A_t S_0 q^_t + sum_{s<=t} (A_t / A_s) (k^_s . q^_t) d_s,
-//     i.e. per 16-column block O = alpha (S_0 Q^T) + D M^T with M the masked,
-//     decay-weighted 16x16 Q K^T of the chunk: three fp32 16x16x4 MFMA
-//     products per chunk (S_0 Q^T and Q K^T while the consumers run the
-//     chunk, D M^T after it).  The output is not on the recurrence's path, so
-//     this takes a third of the per-token work off the serial chain.
-// Consumers and producers meet at two barriers per chunk (one after the
-// consumers have written the chunk's starting state, one at its end).  The L2
-// norm factors are applied to reduced sums and coefficients, so k and q stay
-// raw in LDS.  A run split at a multiple of the chunk length (16 tokens) and
-// resumed from the written-back state gives the same bits as the straight
-// run: the state is folded to its plain form at every chunk start, which is
-// also the form written back, and a chunk's outputs depend only on that state
-// and the chunk's own inputs.
+// The recurrence, per token t of a v-head (state S: key x value),
+//     d_t = b_t (v_t - a_t S_{t-1} k^_t),   S_t = a_t S_{t-1} + k^_t d_t^T,
+//     o_t = S_t^T q^_t
+// (decay first, prediction from the decayed state, output from the updated
+// state), is evaluated sixteen tokens at a time.  With S_0 the state at a
+// chunk's start, A_t the product of the chunk's decays through token t and
+// r(t, s) = A_t / A_s the product of the decays after token s through t,
+//     a_t S_{t-1} k^_t = A_t S_0 k^_t + sum_{s<t} r(t, s) (k^_s . k^_t) d_s,
+// so the chunk's d solve a 16x16 unit lower-triangular system
+//     (I + L) D = R,  L[t][s] = b_t r(t, s) (k^_s . k^_t) (s < t),
+//                     R[t] = b_t (v_t - A_t S_0 k^_t),
+// and then
+//     S_16 = A_15 S_0 + sum_s r(15, s) k^_s d_s^T,
+//     o_t  = A_t S_0^T q^_t + sum_{s<=t} r(t, s) (k^_s . q^_t) d_s.
+// These are the same values the token-by-token recurrence produces (up to
+// rounding); the chunk only changes the order of the arithmetic.  Every
+// product over the key dimension, and the state update over the chunk's
+// tokens, is a dense contraction, so it runs on the matrix cores in three
+// bf16 products per fp32 product: with x = x_hi + x_lo (x_hi the bf16
+// rounding of x, x_lo that of the remainder), a b ~ a_hi b_hi + a_hi b_lo +
+// a_lo b_hi, exact bf16 x bf16 products accumulated in fp32 (operands carry
+// 16 of fp32's 24 significand bits; measured state error ~1e-5 of the
+// state's largest entry, against 1e-4 allowed).  A 16x16x32 bf16 MFMA costs
+// 16 cycles, a 16x16x4 fp32 MFMA (the same fp32 product over 4 keys) 32.
+// The two small 16x16 products of a chunk (T R and M D) stay in fp32.
+//
+// Parallel structure.  A workgroup takes one (sequence, v-head, slice of ISZ
+// value columns); its waves have two roles:
+//   - a state wave owns a block of 16 value columns of the state for the
+//     whole sequence, in MFMA accumulator layout (lane l, register (kb, r):
+//     key 16 kb + 4 (l / 16) + r, column l % 16).  Per chunk it splits the
+//     state into bf16 halves and forms P = K^ S_0 and S_0^T Q^^T (the state
+//     is the B operand of the first and the A operand of the second, so it
+//     never leaves the registers), R, D = T R with T = (I + L)^-1, the
+//     outputs, and the new state.  The q^ / k^ rows in LDS keep their keys in
+//     the order in which a lane supplies them to a 16x16x32 MFMA (keys 32 c +
+//     4 (l / 16) + i and 32 c + 16 + 4 (l / 16) + i, i < 4, side by side), so
+//     a lane's operand is one 16-byte read and matches its state registers;
+//   - four conv waves prepare the chunks: raw inputs loaded into registers a
+//     chunk ahead, conv + SiLU, the L2-normalised q^ and k^ rows and v (per
+//     chunk c); one chunk later the chunk's Gram products k^ k^T and q^ k^T,
+//     L, its inverse T, the output mask M and the decay products are formed:
+//     in a 64-column workgroup a fifth wave forms L and T (so that no wave
+//     carries both the conv and the inversion) and conv waves 1 and 2 form M
+//     and the decay products; in a whole-head one conv waves 0-2 share all
+//     three.  Conv wave 0 also writes each chunk's gates and decay ratios.
+// A chunk is prepared in interval c (conv), finished in c + 1 (T, M, decays)
+// and consumed by the state waves in c + 2; one barrier ends each interval,
+// so q^/k^/v rows are triple-buffered and T, M and the coefficients double-
+// buffered (about 117 KB of LDS at head size 128: one workgroup per CU).  The state is plain at every chunk boundary (no running scale),
+// so a run split at a multiple of 16 tokens and resumed from the written-back
+// state gives the same bits as the straight run.
 //
 // The conv window is rewritten by a second small kernel after this one, so
 // that no workgroup of a sequence can overwrite the window another workgroup
 // of the same sequence has yet to read.
 #include <algorithm>
-#include <type_traits>
+#include <atomic>
 
 #include "device_utils.h"
 #include "gdn_internal.h"
@@ -52,38 +74,47 @@
 namespace gdn {
 namespace {
 
-template <int DK, int DV>
+// SWR: state waves asked for per workgroup (4: slices of 64 value columns, so
+// that a long sequence's heads spread over more CUs; 8: whole 128-column
+// heads, so that a large batch repeats the q/k conv of a head once instead
+// of twice).  Every value is computed the same way in both, bit for bit.
+template <int DK, int DV, int SWR>
 struct PrefillShape {
-    static constexpr int KPL = DK >= 128 ? 16 : (DK >= 32 ? 8 : 4); // keys per consumer lane
-    static constexpr int LPC = DK / KPL;                            // lanes sharing one column
-    static constexpr int CPW = 64 / LPC;                            // columns per consumer wave
-    static constexpr int NCONS = (DV / CPW) < 4 ? (DV / CPW) : 4;   // consumer waves
-    static constexpr int NPROD = 4;                                 // producer waves
-    static constexpr int ISZ = NCONS * CPW;                         // value columns per workgroup
-    static constexpr int NSL = DV / ISZ;                            // workgroups per head
-    static constexpr int NT = 64 * (NCONS + NPROD);
-    static constexpr int CT = 16;                                   // tokens per chunk
-    static constexpr int YS = 2 * DK + ISZ + 4;   // conv outputs per token row (q|k|v slice|pad)
-    static constexpr int SROW = DK + 4;           // starting-state row (one value column), padded
-    static constexpr int NCB = ISZ / 16;          // 16-column output blocks
-    static constexpr int KQ = DK / 4;             // keys per MFMA lane group
-    static constexpr int QKP = DK / 2;            // q (and k) channel pairs
-    static constexpr int NVP = ISZ / 2;           // v channel pairs
-    static constexpr int TPW = CT / NPROD;        // tokens per producer wave
+    static constexpr int CT = 16;              // tokens per chunk: one MFMA tile
+    static constexpr int NKB = DK / 16;        // 16-key blocks of a column block of the state
+    static constexpr int NB = DV / 16;         // 16-column blocks of a head
+    static constexpr int SW = NB < SWR ? NB : SWR; // state waves per workgroup, one block each
+    static constexpr int NSL = NB / SW;        // workgroups per (sequence, v-head)
+    static constexpr int ISZ = 16 * SW;        // value columns per workgroup
+    static constexpr int NPROD = 4;            // conv waves
+    // a wave of its own for the Gram products, T, M and the decay products
+    // when the workgroup is small enough (else the conv waves share them)
+    static constexpr int NFIN = SW <= 4 ? 1 : 0;
+    static constexpr int NT = 64 * (SW + NPROD + NFIN);
+    static constexpr int WPE = (SW + NPROD + NFIN + 3) / 4; // waves per SIMD (one workgroup per CU)
+    static constexpr bool X32 = DK >= 32;      // key products on 16x16x32 (else 16x16x16) MFMAs
+    static constexpr int KG = X32 ? 32 : 16;   // keys per MFMA step
+    static constexpr int NKC = DK / KG;        // MFMA steps over the keys
+    static constexpr int KS = DK + 8;          // row stride of the bf16 q^ / k^ rows (elements)
+    static constexpr int KTS = CT + 8;         // row stride of the bf16 transposed k^ rows
+    static constexpr int TS = CT + 4;          // row stride of 16-wide fp32 rows (floats)
+    static constexpr int QKP = DK / 2;         // q (and k) channel pairs
+    static constexpr int NVP = ISZ / 2;        // v channel pairs
+    static constexpr int TPW = CT / NPROD;     // tokens per producer wave
     static constexpr int NVJ = (TPW * NVP + 63) / 64; // v conv jobs per producer lane
-    // Q K^T is split over the producer waves without an output block: GP
-    // parts of the key range (a power of two dividing the KQ / 4 steps)
-    static constexpr int GFREE = NPROD - NCB;
-    static constexpr int GP = (GFREE >= 4 && (KQ / 4) % 4 == 0) ? 4
-                            : (GFREE >= 2 && (KQ / 4) % 2 == 0) ? 2 : 1;
     static_assert(DK == DV, "square heads only");
-    static_assert(KPL % 4 == 0 && DK % KPL == 0 && LPC >= 1 && LPC <= 64, "key split");
-    static_assert(NCONS >= 1 && DV % ISZ == 0 && ISZ % 16 == 0, "column split");
-    static_assert(CT == 16, "a chunk is one 16-wide MFMA tile and one 16-lane DPP row");
-    static_assert(NCB <= NPROD, "each producer wave keeps at most one output block");
+    static_assert(DK % 16 == 0 && NB % SW == 0, "16-wide blocks");
     static_assert(QKP <= 64, "one q/k channel pair per producer lane");
-    static_assert(KQ % 4 == 0, "MFMA operands are read as float4 runs");
 };
+
+// Per-chunk coefficients (rows of cf[2][CF_N][16]): for token t of the chunk
+//   CF_B   b_t (0 past the sequence's end)
+//   CF_A   A_t, the product of the chunk's decays through t
+//   CF_E   r(15, t), the decay from after t to the chunk's end
+//   CF_EM  r(m - 1, t) for t < m, else 0, when a checkpoint falls after the
+//          chunk's first m < 16 tokens
+//   CF_SC  [0] A_15, [1] A_{m-1} (the checkpoint's decay)
+constexpr int CF_B = 0, CF_A = 1, CF_E = 2, CF_EM = 3, CF_SC = 4, CF_N = 5;
 
 struct PrefillParams {
     uint8_t* layer;
@@ -142,16 +173,6 @@ __device__ __forceinline__ int seq_at_position(const int32_t* cu, int N, int r)
     return __ffsll(static_cast<long long>(hit)) - 1;
 }
 
-// The scale of the state is folded into it once it falls below 2^-40 (bits
-// of the float), so s stays within 2^40 of the state's magnitude.
-constexpr uint32_t kFoldBelow = (127u - 40u) << 23;
-
-// A token's coefficients in LDS (floats):
-//   SC_SCALED  c rk, b, rk / c, c     (c: running product of the chunk's
-//                                     decays through the token)
-//   SC_PLAIN   a, b, rk, rq           (chunks that may need a fold)
-constexpr int SC_SCALED = 0, SC_PLAIN = 4, SC_N = 8;
-
 constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer resource, gfx9-family layout
 
 // A buffer resource's range from a wave-uniform byte count, capped at
@@ -172,33 +193,106 @@ __device__ __forceinline__ float row_shr_or_one(float v)
                                                       0x110 + N, 0xF, 0xF, false));
 }
 
+// D = A B + C on a 16x16x4 fp32 tile: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16] and holds D[4 (l / 16) + r][l % 16] in register r.
 __device__ __forceinline__ v4f mfma16(float a, float b, v4f c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int DK, int DV, int W>
-// four waves per SIMD: two 512-thread workgroups per CU (their LDS fits too)
-__global__ __launch_bounds__((PrefillShape<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4)))
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short bf16x4 __attribute__((ext_vector_type(4))); // bit patterns
+
+// 16x16x32 bf16: lane l supplies A[l % 16][8 (l / 16) + i] and
+// B[8 (l / 16) + i][l % 16], i < 8; 16x16x16 bf16: A[l % 16][4 (l / 16) + i]
+// and B[4 (l / 16) + i][l % 16], i < 4; both hold D as mfma16 does.  (Lane
+// layouts and costs measured on gfx950: 16 cycles each, 32 for mfma16.)
+__device__ __forceinline__ v4f mfma_k32(bf16x8 a, bf16x8 b, v4f c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma_k16(bf16x4 a, bf16x4 b, v4f c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x)
+{
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); // nearest, ties to even
+}
+// x = hi + lo to 16 significand bits: hi the bf16 rounding of x, lo that of
+// the (exact) remainder
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo)
+{
+    hi = bf16_bits(x);
+    lo = bf16_bits(x - __uint_as_float(uint32_t(hi) << 16));
+}
+
+// The three products of a x b in bf16 halves (the lo x lo term, 2^-16 of it,
+// is dropped): a_hi b_hi + a_hi b_lo + a_lo b_hi.
+__device__ __forceinline__ v4f mfma3_k32(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, v4f c)
+{
+    c = mfma_k32(ah, bh, c);
+    c = mfma_k32(ah, bl, c);
+    return mfma_k32(al, bh, c);
+}
+__device__ __forceinline__ v4f mfma3_k16(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl, v4f c)
+{
+    c = mfma_k16(ah, bh, c);
+    c = mfma_k16(ah, bl, c);
+    return mfma_k16(al, bh, c);
+}
+
+// LDS values one lane of a wave wrote, read by other lanes of the same wave:
+// a wave's LDS operations complete in order, so waiting for its own LDS
+// operations (lgkmcnt 0, not its outstanding global loads) and keeping the
+// compiler from moving code across suffices.
+__device__ __forceinline__ void lds_wave_sync()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F); // vmcnt and expcnt at their maximum: no wait
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Position of key `key` in a bf16 q^ / k^ row: 32-key groups where lane
+// group q of a 16x16x32 MFMA finds its keys 4 q + i and 16 + 4 q + i (i < 4)
+// at 8 q .. 8 q + 7; plain order for 16-key heads.
+template <bool X32>
+__device__ __forceinline__ int key_pos(int key)
+{
+    if constexpr (X32)
+        return 32 * (key >> 5) + 8 * ((key >> 2) & 3) + 4 * ((key >> 4) & 1) + (key & 3);
+    else
+        return key;
+}
+
+template <int DK, int DV, int W, int SWR>
+// one workgroup per CU (its LDS)
+__global__ __launch_bounds__((PrefillShape<DK, DV, SWR>::NT))
+__attribute__((amdgpu_waves_per_eu(PrefillShape<DK, DV, SWR>::WPE)))
 void prefill_kernel(PrefillParams p)
 {
-    using Sh = PrefillShape<DK, DV>;
-    constexpr int KPL = Sh::KPL, LPC = Sh::LPC, CPW = Sh::CPW, NCONS = Sh::NCONS;
-    constexpr int ISZ = Sh::ISZ, CT = Sh::CT, YS = Sh::YS, SROW = Sh::SROW, NCB = Sh::NCB;
-    constexpr int KQ = Sh::KQ, QKP = Sh::QKP, NVP = Sh::NVP, TPW = Sh::TPW, NVJ = Sh::NVJ;
+    using Sh = PrefillShape<DK, DV, SWR>;
+    constexpr int CT = Sh::CT, NKB = Sh::NKB, SW = Sh::SW, ISZ = Sh::ISZ, KS = Sh::KS;
+    constexpr int TS = Sh::TS, QKP = Sh::QKP, NVP = Sh::NVP, TPW = Sh::TPW, NVJ = Sh::NVJ;
+    static_assert(KS % 8 == 0 && Sh::KTS % 4 == 0, "16- and 8-byte operand reads");
 
-    // Chunk k's inputs are written while chunk k-1 runs, read by the
-    // consumers and the products while it runs, and its coefficients once more
-    // by its epilogue while chunk k+1 runs, when chunk k+2 is being prepared:
-    // hence two buffers for the conv outputs and three for the coefficients.
-    __shared__ __align__(16) float ys[2][CT][YS];      // conv outputs (raw q | raw k | v)
-    __shared__ __align__(16) float s0[ISZ][SROW];      // the state at the current chunk's start
-    __shared__ __align__(16) float sc[3][CT][SC_N];    // per token coefficients (SC_*)
-    __shared__ __align__(16) float alf[3][CT];         // output scale A_t rq_t per token
-    __shared__ __align__(16) float dbuf[2][CT][ISZ];   // d per (token, value column)
-    __shared__ __align__(16) float gq[2][Sh::GP][CT][CT]; // parts of a chunk's Q K^T
-    __shared__ __align__(16) v4f pq[2][NCB][64];        // S_0 Q^T of a block, MFMA lane order
-    __shared__ uint32_t nofold[3];                     // the chunk's decays need no fold
+    // chunk c's rows are written in interval c, read by the Gram stage in
+    // c + 1 and by the state waves in c + 2: three buffers; T, M and the
+    // coefficients are written in c + 1 and read in c + 2: two buffers
+    // bf16 halves of the q^ / k^ rows ([hi, lo][token][key position]) and of
+    // the k^ columns ([hi, lo][key][token]) for the state update
+    __shared__ __align__(16) uint16_t kr[3][2][CT][KS]; // k^ (L2-normalised)
+    __shared__ __align__(16) uint16_t qr[3][2][CT][KS]; // q^ (normalised, times scale)
+    __shared__ __align__(16) uint16_t kc[3][2][DK][Sh::KTS];
+    __shared__ __align__(16) float vt[3][ISZ][TS];  // v of the slice, [column][token]
+    __shared__ __align__(16) float gt[2][2][CT];    // decay (1 past the end), beta (0 past it)
+    __shared__ __align__(16) float rt[2][CT][TS];   // r(t, s) for s < t, 1 for s >= t
+    __shared__ __align__(16) float tm[2][CT][TS];   // T = (I + L)^-1
+    __shared__ __align__(16) float mm[2][CT][TS];   // M[t][s] = r(t, s) q^_t . k^_s (s <= t)
+    __shared__ __align__(16) float cf[2][CF_N][CT]; // CF_* rows
+    __shared__ __align__(16) float lw[CT][TS];      // L of the chunk being inverted
+    // conv taps of the slice's channel pairs, [tap][q pairs | k pairs | v pairs]
+    __shared__ __align__(16) float2 taps[W][2 * QKP + NVP];
 
     // workgroup -> (k-head g, dispatch position of sequence n, v-head of the
     // group, slice): the workgroups of one (n, g) read the same q/k inputs and
@@ -218,6 +312,7 @@ void prefill_kernel(PrefillParams p)
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform: role and token
     const int lane = tid & 63;                                 // indices go to scalar registers
+    const int m16 = lane % 16, q4 = lane / 16;
     // a sequence whose range is empty or not inside [0, total_tokens) is skipped
     const int64_t tb64 = p.cu[n], te64 = p.cu[n + 1];
     if (tb64 < 0 || te64 <= tb64 || te64 > p.total_tokens)
@@ -237,6 +332,22 @@ void prefill_kernel(PrefillParams p)
     const bool warm = p.hs[n] != 0;
     uint8_t* page = p.layer + int64_t(slot) * p.page_stride;
     const int nchunks = (L + CT - 1) / CT;
+    auto chunk_len = [&](int k) { return min(CT, L - k * CT); };
+
+    // checkpoint: the state after the first ck_len tokens, into another page
+    int ck_c = -1, ck_m = CT; // its chunk, and how many of the chunk's tokens it includes
+    float* ck_tile = nullptr;
+    if (p.ckpt_slot) {
+        const int cs = p.ckpt_slot[n], cl = p.ckpt_len[n];
+        if (cs >= 0 && cs < p.num_slots && cl >= 1 && cl <= L) {
+            ck_c = (cl - 1) / CT;
+            ck_m = cl - ck_c * CT;
+            ck_tile = reinterpret_cast<float*>(p.layer + int64_t(cs) * p.page_stride + p.ssm_off) +
+                      int64_t(h) * DK * DV;
+        }
+    }
+    // a checkpoint strictly inside its chunk needs the state after ck_m tokens
+    const bool ck_mid = ck_c >= 0 && ck_m < chunk_len(ck_c);
 
     // global channel of the workgroup's channel `ch` (q | k | v slice)
     auto chan = [&](int ch) -> int {
@@ -246,213 +357,311 @@ void prefill_kernel(PrefillParams p)
             return p.Hk * DK + g * DK + (ch - DK);
         return 2 * p.Hk * DK + h * DV + sl * ISZ + (ch - 2 * DK);
     };
-    auto chunk_len = [&](int k) { return min(CT, L - k * CT); };
 
-    if (wave < NCONS) {
-        // ======================= consumer waves =============================
-        // (each consumer shares its SIMD with a producer wave; the two roles'
-        // work per chunk is balanced, so neither takes issue priority)
-        const int col = wave * CPW + lane / LPC; // value column inside the slice
-        const int jl = lane % LPC;
-        const int gcol = sl * ISZ + col;
+    // Gates of token k CT + lane % CT of head h (zero past the sequence's end):
+    // buffer loads whose range check covers the sequence's tokens only.
+    auto load_gates = [&](int k) {
+        const int ht = p.Hv * 4;
+        const int64_t g0 = int64_t(tb + k * CT) * p.Hv + h;
+        const int grec = range_bytes(int64_t(L - k * CT) * ht);
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(p.alpha) + g0, short(0), grec, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(p.beta) + g0, short(0), grec, kBufferWord3);
+        return make_float2(
+            __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, (lane % CT) * ht, 0, 0)),
+            __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (lane % CT) * ht, 0, 0)));
+    };
+    // Chunk k's gates and decay ratios into gt / rt[k & 1] from the gates of
+    // its tokens (lane l: token l % 16 of row l / 16); tokens past the end
+    // take decay 1 and beta 0.  r(t, s), the product of the decays after s
+    // through t: for s = 4 j + (row), an inclusive scan over t of the decays
+    // with the tokens up to s replaced by 1.
+    auto write_ratios = [&](int k, float2 gate) {
+        const int b2 = k & 1;
+        const int nt = chunk_len(k);
+        const int t_ = m16;
+        const float at = t_ < nt ? gate.x : 1.f;
+        if (lane < CT) {
+            gt[b2][0][t_] = at;
+            gt[b2][1][t_] = t_ < nt ? gate.y : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s_ = 4 * j + q4;
+            float x = t_ > s_ ? at : 1.f;
+            x *= row_shr_or_one<1>(x);
+            x *= row_shr_or_one<2>(x);
+            x *= row_shr_or_one<4>(x);
+            x *= row_shr_or_one<8>(x);
+            rt[b2][t_][s_] = x;
+        }
+    };
+
+    // Chunk k's T, M and coefficients (interval k + 1), from its rows, gates
+    // and decay ratios, in three parts: (0) L from the Gram matrix k^ k^T and
+    // T = (I + L)^-1 by forward substitution, (1) M from q^ k^T, (2) the decay
+    // products.  Part 0 writes and reads back lw within one wave.
+    auto finish = [&](int k, int part) {
+        if (k >= nchunks || part >= 3)
+            return;
+        const int b3 = k % 3, b2 = k & 1;
+        const int pw = part;
+        if (pw <= 1) {
+            // Gram: G[t][s] = x_t . k^_s, x = k^ (wave 0) or q^ (wave 1);
+            // register r: t = 4 q4 + r, s = m16 (rows are A and B operands
+            // alike: lane l reads row l % 16)
+            const uint16_t(*xh)[KS] = pw == 0 ? kr[b3][0] : qr[b3][0];
+            const uint16_t(*xl)[KS] = pw == 0 ? kr[b3][1] : qr[b3][1];
+            v4f gm = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (Sh::X32) {
+#pragma unroll
+                for (int c2 = 0; c2 < Sh::NKC; ++c2) {
+                    const int kp = 32 * c2 + 8 * q4;
+                    auto ld8 = [&](const uint16_t* row) {
+                        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + kp));
+                    };
+                    gm = mfma3_k32(ld8(xh[m16]), ld8(xl[m16]), ld8(kr[b3][0][m16]),
+                                   ld8(kr[b3][1][m16]), gm);
+                }
+            } else {
+                auto ld4 = [&](const uint16_t* row) {
+                    return __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(row + 4 * q4));
+                };
+                gm = mfma3_k16(ld4(xh[m16]), ld4(xl[m16]), ld4(kr[b3][0][m16]), ld4(kr[b3][1][m16]), gm);
+            }
+            const int s_ = m16;
+            if (pw == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t_ = 4 * q4 + r;
+                    lw[t_][s_] = s_ < t_ ? gt[b2][1][t_] * rt[b2][t_][s_] * gm[r] : 0.f;
+                }
+                // the wave's own LDS writes above are read back by other lanes
+                lds_wave_sync();
+                // T = (I + L)^-1, column j = m16 in lane j (lanes 16-63 repeat it);
+                // the column index is opaque here so that the sixteen entries of
+                // the identity column are formed per chunk, not held across the
+                // chunk loop
+                int jc = m16;
+                asm volatile("" : "+v"(jc));
+                // T[t][j] = [t == j] - sum_{u<t} L[t][u] T[u][j]
+                float tc[CT];
+#pragma unroll
+                for (int t_ = 0; t_ < CT; ++t_) {
+                    float acc = t_ == jc ? 1.f : 0.f;
+#pragma unroll
+                    for (int u = 0; u < t_; ++u)
+                        acc = fmaf(-lw[t_][u], tc[u], acc);
+                    tc[t_] = acc;
+                }
+                if (lane < CT) {
+#pragma unroll
+                    for (int t_ = 0; t_ < CT; ++t_)
+                        tm[b2][t_][lane] = tc[t_];
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t_ = 4 * q4 + r;
+                    mm[b2][t_][s_] = s_ <= t_ ? rt[b2][t_][s_] * gm[r] : 0.f;
+                }
+            }
+        } else if (lane < CT) {
+            // wave 2: A_t = a_0 r(t, 0), r(15, t), the checkpoint's r(m - 1, t)
+            const int t_ = lane;
+            const float a0 = gt[b2][0][0];
+            cf[b2][CF_B][t_] = gt[b2][1][t_];
+            cf[b2][CF_A][t_] = a0 * rt[b2][t_][0];
+            cf[b2][CF_E][t_] = rt[b2][CT - 1][t_];
+            cf[b2][CF_EM][t_] = t_ < ck_m ? rt[b2][ck_m - 1][t_] : 0.f;
+            if (t_ == 0) {
+                cf[b2][CF_SC][0] = a0 * rt[b2][CT - 1][0];
+                cf[b2][CF_SC][1] = a0 * rt[b2][ck_m - 1][0];
+            }
+        }
+    };
+
+    if (wave < SW) {
+        // ========================= state waves ==============================
+        const int col0 = sl * ISZ + 16 * wave; // first column of the block in the head
         float* tile = reinterpret_cast<float*>(page + p.ssm_off) + int64_t(h) * DK * DV;
-        float s[KPL];
+        // s[kb][r] = S[key 16 kb + 4 q4 + r][column col0 + m16], at byte
+        // eoff + (16 kb + r) DV 4 of the head's tile.  State I/O goes through
+        // buffer resources with the whole offset in the lane's VGPR, so that
+        // the (rare) checkpoint stores inside the chunk loop hold one resource
+        // and no addresses across it.
+        const int eoff = ((4 * q4) * DV + col0 + m16) * 4;
+        constexpr int kTileBytes = DK * DV * 4;
+        v4f s[NKB];
 #pragma unroll
-        for (int m = 0; m < KPL / 4; ++m)
+        for (int kb = 0; kb < NKB; ++kb)
+            s[kb] = v4f{0.f, 0.f, 0.f, 0.f};
+        const __amdgpu_buffer_rsrc_t rt_tile =
+            __builtin_amdgcn_make_buffer_rsrc(tile, short(0), kTileBytes, kBufferWord3);
+        if (warm) { // a cold page is never read
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                s[4 * m + e] = warm ? tile[(4 * jl + 4 * LPC * m + e) * DV + gcol] : 0.f;
-        // d of tokens past a ragged chunk's end meets zeros in M; it must be
-        // finite, so the buffers start at zero
-        for (int e = tid; e < 2 * CT * ISZ; e += 64 * NCONS)
-            (&dbuf[0][0][0])[e] = 0.f;
-        // operands of one token; the next token's are fetched from LDS while
-        // the current one is computed
-        struct Ops {
-            float4 k[KPL / 4];
-            float4 g; // SC_SCALED or SC_PLAIN
-            float v;
-        };
-        auto fetch = [&](Ops& r, int buf, int sb, int tt, auto checked) {
-            const float* yt = ys[buf][tt];
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int m = 0; m < KPL / 4; ++m)
-                r.k[m] = *reinterpret_cast<const float4*>(yt + DK + 4 * jl + 4 * LPC * m);
-            r.g = *reinterpret_cast<const float4*>(
-                &sc[sb][tt][decltype(checked)::value ? SC_PLAIN : SC_SCALED]);
-            r.v = yt[2 * DK + col];
-        };
-        // The state is held as cs * s: the decays of a chunk's tokens gather in
-        // the lane-uniform scale cs, so a token's update is one fma per
-        // element.  The scale is folded back into s at the start of every
-        // chunk, and at once should it fall below kFoldBelow.
-        float cs = 1.f;
-        auto fold = [&](float c) {
-#pragma unroll
-            for (int m = 0; m < KPL; ++m)
-                s[m] *= c;
-        };
-        // `checked`: whether the scale may have to be folded within the chunk.
-        // The producers rule that out for most chunks; the scale after each of
-        // their tokens is then the running product of the chunk's decays,
-        // which they also fold into the token's coefficients.
-        auto step = [&](const Ops& r, int buf, int tt, auto checked) {
-            constexpr bool kChecked = decltype(checked)::value;
-            const float b = r.g.y;
-            float ca, cu, rkc; // a S_old = ca s; ca rk; rk / ca
-            if constexpr (kChecked) {
-                ca = cs * r.g.x;
-                if ((__builtin_amdgcn_readfirstlane(__float_as_uint(ca)) & 0x7FFFFFFFu) <
-                    kFoldBelow) {
-                    fold(ca);
-                    ca = 1.f;
-                }
-                cu = ca * r.g.z;
-                rkc = r.g.z * __builtin_amdgcn_rcpf(ca);
-            } else {
-                ca = r.g.w;
-                cu = r.g.x;
-                rkc = r.g.z;
-            }
-            float u0 = 0.f, u1 = 0.f;
-#pragma unroll
-            for (int m = 0; m < KPL / 4; ++m) {
-                u0 = fmaf(s[4 * m + 0], r.k[m].x, u0);
-                u1 = fmaf(s[4 * m + 1], r.k[m].y, u1);
-                u0 = fmaf(s[4 * m + 2], r.k[m].z, u0);
-                u1 = fmaf(s[4 * m + 3], r.k[m].w, u1);
-            }
-            const float u = group_sum<LPC>(u0 + u1); // s k (raw k)
-            const float d = b * (r.v - cu * u);      // b (v - a S_old k^)
-            // S <- a S_old + d k^ k^T = ca (s + (d rk / ca) k)
-            const float dk = d * rkc;
-#pragma unroll
-            for (int m = 0; m < KPL / 4; ++m) {
-                s[4 * m + 0] = fmaf(dk, r.k[m].x, s[4 * m + 0]);
-                s[4 * m + 1] = fmaf(dk, r.k[m].y, s[4 * m + 1]);
-                s[4 * m + 2] = fmaf(dk, r.k[m].z, s[4 * m + 2]);
-                s[4 * m + 3] = fmaf(dk, r.k[m].w, s[4 * m + 3]);
-            }
-            cs = ca;
-            // the LPC lanes of the column hold the same bits (each step of
-            // group_sum adds the same two values in every lane), so all of
-            // them store it: no exec-mask switch per token
-            dbuf[buf][tt][col] = d;
-        };
-        // checkpoint emission: the state after token ck_tok (if any) is also
-        // stored into the checkpoint page
-        // (buffer stores: one VGPR offset per lane and per-store constants, so
-        // the rarely used path holds no addresses across the token loop)
-        int ck_tok = -1;
-        float* ck_tile = tile;
-        if (p.ckpt_slot) {
-            const int cs = p.ckpt_slot[n], cl = p.ckpt_len[n];
-            if (cs >= 0 && cs < p.num_slots && cl >= 1 && cl <= L) {
-                ck_tok = cl - 1;
-                ck_tile = reinterpret_cast<float*>(p.layer + int64_t(cs) * p.page_stride + p.ssm_off) +
-                          int64_t(h) * DK * DV;
-            }
+                for (int r = 0; r < 4; ++r)
+                    s[kb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        rt_tile, eoff + (16 * kb + r) * DV * 4, 0, 0));
         }
-        // the chunk holding the checkpoint token (-1: none; -1 / CT would be 0)
-        const int ck_chunk = ck_tok >= 0 ? ck_tok / CT : -1;
-        const __amdgpu_buffer_rsrc_t ck_rs = __builtin_amdgcn_make_buffer_rsrc(
-            ck_tile, short(0), ck_tok >= 0 ? DK * DV * 4 : 0, 0x00020000);
-        const int voff = (4 * jl * DV + gcol) * 4;
-        auto store_ck = [&]() {
+        auto store_state = [&](__amdgpu_buffer_rsrc_t dst, const v4f (&x)[NKB]) {
 #pragma unroll
-            for (int m = 0; m < KPL / 4; ++m)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        __float_as_uint(s[4 * m + e] * cs), ck_rs,
-                        voff + (4 * LPC * m + e) * DV * 4, 0, 0);
+                for (int r = 0; r < 4; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[kb][r]), dst,
+                                                          eoff + (16 * kb + r) * DV * 4, 0, 0);
         };
-        __syncthreads(); // B: chunk 0 prepared, d buffers cleared
-        for (int c = 0; c < nchunks; ++c) {
-            const int buf = c & 1, sb = c % 3;
-            const int nt = chunk_len(c);
-            fold(cs);
-            cs = 1.f;
-            // the chunk's starting state, for the producers' output products
+        const __amdgpu_buffer_rsrc_t rt_ck = __builtin_amdgcn_make_buffer_rsrc(
+            ck_tile ? ck_tile : tile, short(0), ck_tile ? kTileBytes : 0, kBufferWord3);
+        __syncthreads(); // the producers' taps are in LDS
+        for (int c = 0; c < nchunks + 2; ++c) {
+            const int k = c - 2;
+            if (k >= 0) {
+                const int b3 = k % 3, b2 = k & 1;
+                const int nt = chunk_len(k);
+                // P[t][col] = k^_t . S_0[:, col]  (register r: token 4 q4 + r)
+                // O[col][t] = S_0[:, col] . q^_t  (register r: column 4 q4 + r, token m16)
+                v4f P = {0.f, 0.f, 0.f, 0.f}, O = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (Sh::X32) {
 #pragma unroll
-            for (int m = 0; m < KPL / 4; ++m)
-                *reinterpret_cast<float4*>(&s0[col][4 * jl + 4 * LPC * m]) =
-                    make_float4(s[4 * m], s[4 * m + 1], s[4 * m + 2], s[4 * m + 3]);
-            __syncthreads(); // X: starting state written
-            // the producers' verdict: no token of the chunk needs a fold
-            const bool quiet = __builtin_amdgcn_readfirstlane(nofold[sb]) != 0u;
-            Ops A, B;
-            auto per_token = [&](auto checked) {
-                for (int tt = 0; tt < nt; ++tt) {
-                    fetch(A, buf, sb, tt, checked);
-                    step(A, buf, tt, checked);
-                    if (c * CT + tt == ck_tok)
-                        store_ck();
-                }
-            };
-            if (nt == CT && ck_chunk != c && quiet) {
-                // full chunk: a fully unrolled loop without branches (every LDS
-                // address is a base plus an immediate), in which the operands of
-                // token t+1 are requested before token t is computed; the
-                // scheduling barriers keep the compiler from sinking those reads
-                // next to their use, so each token waits only for reads issued
-                // a whole token earlier (the last fetch of the chunk re-reads
-                // token CT-1 and is unused)
-                constexpr std::false_type scaled{};
-                fetch(A, buf, sb, 0, scaled);
+                    for (int c2 = 0; c2 < Sh::NKC; ++c2) {
+                        // the lane's 8 keys of the step: 32 c2 + 4 q4 + i, 32 c2 + 16 + 4 q4 + i
+                        bf16x8 sh, sl;
 #pragma unroll
-                for (int tt = 0; tt < CT; tt += 2) {
-                    fetch(B, buf, sb, tt + 1, scaled);
-                    __builtin_amdgcn_sched_barrier(0);
-                    step(A, buf, tt, scaled);
-                    fetch(A, buf, sb, min(tt + 2, CT - 1), scaled);
-                    __builtin_amdgcn_sched_barrier(0);
-                    step(B, buf, tt + 1, scaled);
+                        for (int i = 0; i < 8; ++i) {
+                            uint16_t hi, lo;
+                            split_bf16(s[2 * c2 + i / 4][i % 4], hi, lo);
+                            sh[i] = __builtin_bit_cast(__bf16, hi);
+                            sl[i] = __builtin_bit_cast(__bf16, lo);
+                        }
+                        const int kp = 32 * c2 + 8 * q4;
+                        auto ld8 = [&](const uint16_t* row) {
+                            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + kp));
+                        };
+                        P = mfma3_k32(ld8(kr[b3][0][m16]), ld8(kr[b3][1][m16]), sh, sl, P);
+                        O = mfma3_k32(sh, sl, ld8(qr[b3][0][m16]), ld8(qr[b3][1][m16]), O);
+                    }
+                } else {
+                    bf16x4 sh, sl;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        uint16_t hi, lo;
+                        split_bf16(s[0][i], hi, lo);
+                        sh[i] = short(hi);
+                        sl[i] = short(lo);
+                    }
+                    auto ld4 = [&](const uint16_t* row) {
+                        return __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(row + 4 * q4));
+                    };
+                    P = mfma3_k16(ld4(kr[b3][0][m16]), ld4(kr[b3][1][m16]), sh, sl, P);
+                    O = mfma3_k16(sh, sl, ld4(qr[b3][0][m16]), ld4(qr[b3][1][m16]), O);
                 }
-            } else if (quiet) { // a ragged last chunk, or the chunk holding the checkpoint token
-                per_token(std::false_type{});
-            } else {
-                per_token(std::true_type{});
+                // R[t] = b_t (v_t - A_t P_t), then D = T R
+                const float4 bb = *reinterpret_cast<const float4*>(&cf[b2][CF_B][4 * q4]);
+                const float4 aa = *reinterpret_cast<const float4*>(&cf[b2][CF_A][4 * q4]);
+                const float4 vv = *reinterpret_cast<const float4*>(&vt[b3][16 * wave + m16][4 * q4]);
+                const float4 tt = *reinterpret_cast<const float4*>(&tm[b2][m16][4 * q4]);
+                const float R0 = bb.x * (vv.x - aa.x * P[0]);
+                const float R1 = bb.y * (vv.y - aa.y * P[1]);
+                const float R2 = bb.z * (vv.z - aa.z * P[2]);
+                const float R3 = bb.w * (vv.w - aa.w * P[3]);
+                v4f d = {0.f, 0.f, 0.f, 0.f}; // d[r] = d_{4 q4 + r}[col0 + m16]
+                d = mfma16(tt.x, R0, d);
+                d = mfma16(tt.y, R1, d);
+                d = mfma16(tt.z, R2, d);
+                d = mfma16(tt.w, R3, d);
+                // outputs: O^T = A_t O^T + D^T M^T (lane: 4 columns of token m16)
+                const float4 mv = *reinterpret_cast<const float4*>(&mm[b2][m16][4 * q4]);
+                O *= cf[b2][CF_A][m16];
+                O = mfma16(d[0], mv.x, O);
+                O = mfma16(d[1], mv.y, O);
+                O = mfma16(d[2], mv.z, O);
+                O = mfma16(d[3], mv.w, O);
+                if (m16 < nt)
+                    *reinterpret_cast<uint2*>(out_base + int64_t(k * CT + m16) * out_tok +
+                                              16 * wave + 4 * q4) = pack_bf16x4(O[0], O[1], O[2], O[3]);
+                // S <- A_15 S_0 + sum_s r(15, s) k^_s d_s^T (and, for a checkpoint
+                // inside the chunk, the state after its first ck_m tokens): per
+                // 16-key block, K^T (16 keys x 16 tokens) times the decayed D
+                auto advance = [&](v4f (&x)[NKB], float a0, const float4& e) {
+                    bf16x4 dh, dl;
+                    const float de[4] = {d[0] * e.x, d[1] * e.y, d[2] * e.z, d[3] * e.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        uint16_t hi, lo;
+                        split_bf16(de[i], hi, lo);
+                        dh[i] = short(hi);
+                        dl[i] = short(lo);
+                    }
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) {
+                        const bf16x4 kh4 = __builtin_bit_cast(
+                            bf16x4, *reinterpret_cast<const uint2*>(&kc[b3][0][16 * kb + m16][4 * q4]));
+                        const bf16x4 kl4 = __builtin_bit_cast(
+                            bf16x4, *reinterpret_cast<const uint2*>(&kc[b3][1][16 * kb + m16][4 * q4]));
+                        x[kb] = mfma3_k16(kh4, kl4, dh, dl, s[kb] * a0);
+                    }
+                };
+                if (k == ck_c && ck_mid) {
+                    v4f sc[NKB];
+                    advance(sc, cf[b2][CF_SC][1],
+                            *reinterpret_cast<const float4*>(&cf[b2][CF_EM][4 * q4]));
+                    store_state(rt_ck, sc);
+                }
+                advance(s, cf[b2][CF_SC][0], *reinterpret_cast<const float4*>(&cf[b2][CF_E][4 * q4]));
+                if (k == ck_c && !ck_mid)
+                    store_state(rt_ck, s);
             }
-            __syncthreads(); // P: chunk done
+            __syncthreads(); // end of interval c
         }
-#pragma unroll
-        for (int m = 0; m < KPL / 4; ++m)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                tile[(4 * jl + 4 * LPC * m + e) * DV + gcol] = s[4 * m + e] * cs;
+        store_state(rt_tile, s);
+        return;
+    }
+
+    if (Sh::NFIN && wave == SW + Sh::NPROD) {
+        // ========================= finish wave ==============================
+        __syncthreads(); // the conv waves' taps are in LDS
+        for (int c = 0; c < nchunks + 2; ++c) {
+            if (c >= 1)
+                finish(c - 1, 0);
+            __syncthreads(); // end of interval c
+        }
         return;
     }
 
     // ========================= producer waves ===============================
-    const int pw = wave - Sh::NCONS;
+    const int pw = wave - SW;
     const uint16_t* win = reinterpret_cast<const uint16_t*>(page + p.conv_off);
 
-    // conv taps and bias of the lane's channel pairs: q and k pair `lane`
-    // (lanes past DK/2 idle), v pair of each of the lane's v jobs
-    float wq[2][W], wk[2][W], wv[NVJ][2][W];
-    float bq[2], bk[2], bv[NVJ][2];
-    auto load_taps = [&](int ch, float (&w2)[2][W], float (&b2)[2]) {
+    // conv taps of the slice's channel pairs into LDS (read back per chunk, so
+    // that they hold no registers across the loop); biases stay in registers
+    for (int e = tid - 64 * SW; e < W * (2 * QKP + NVP); e += 64 * Sh::NPROD) {
+        const int w = e / (2 * QKP + NVP), pr = e - w * (2 * QKP + NVP);
+        const int ch = pr < QKP ? 2 * pr : (pr < 2 * QKP ? DK + 2 * (pr - QKP) : 2 * DK + 2 * (pr - 2 * QKP));
         const int c = chan(ch);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int w = 0; w < W; ++w)
-                w2[i][w] = bf16_to_f32(p.conv_w[int64_t(c + i) * W + w]);
-            b2[i] = p.conv_b ? bf16_to_f32(p.conv_b[c + i]) : 0.f;
-        }
+        taps[w][pr] = make_float2(bf16_to_f32(p.conv_w[int64_t(c) * W + w]),
+                                  bf16_to_f32(p.conv_w[int64_t(c + 1) * W + w]));
+    }
+    auto bias2 = [&](int ch) {
+        const int c = chan(ch);
+        return p.conv_b ? make_float2(bf16_to_f32(p.conv_b[c]), bf16_to_f32(p.conv_b[c + 1]))
+                        : make_float2(0.f, 0.f);
     };
     const int qkp = min(lane, QKP - 1); // q/k pair of the lane (clamped; idle lanes recompute)
-    load_taps(2 * qkp, wq, bq);
-    load_taps(DK + 2 * qkp, wk, bk);
+    const float2 bq = bias2(2 * qkp), bk = bias2(DK + 2 * qkp);
     // v job jj of the lane: token t0 + vi[jj] of the wave's TPW, pair vpj[jj]
     int vi[NVJ], vpj[NVJ];
+    float2 bv[NVJ];
 #pragma unroll
     for (int jj = 0; jj < NVJ; ++jj) {
         const int j = lane + 64 * jj;
         vi[jj] = j / NVP;
         vpj[jj] = j % NVP;
-        load_taps(2 * DK + 2 * vpj[jj], wv[jj], bv[jj]);
+        bv[jj] = bias2(2 * DK + 2 * vpj[jj]);
     }
 
     // Raw inputs of chunk k for this wave's TPW tokens, loaded into registers
@@ -460,9 +669,10 @@ void prefill_kernel(PrefillParams p)
     // before the wave's first token and its TPW rows; for v the W rows of each
     // job; the gates of token k CT + lane % CT.  All are buffer loads with the
     // row in the lane's offset: the range check returns zero for rows past
-    // the sequence's end (their results are never stored) and for the rows
-    // before its start when the sequence is cold, whose window resource is
-    // empty, so no load waits on a branch and a cold page is never read.
+    // the sequence's end and for the rows before its start when the sequence
+    // is cold, whose window resource is empty, so no load waits on a branch
+    // and a cold page is never read.  Rows past the end give finite values
+    // whose tokens the coefficients then leave out (b = 0, decay 1).
     constexpr int HR = W - 1, NR = HR + TPW;
     constexpr uint32_t kOutOfRange = 0xFFFFFFF0u; // past any num_records below
     const int t0 = pw * TPW;
@@ -521,69 +731,77 @@ void prefill_kernel(PrefillParams p)
                 }
             }
         }
-        // gates of token k CT + lane % CT (zero past the sequence's end)
-        const int ht = p.Hv * 4;
-        const int64_t g0 = int64_t(tb + k * CT) * p.Hv + h;
-        const int grec = range_bytes(int64_t(L - k * CT) * ht);
-        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(p.alpha) + g0, short(0), grec, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(p.beta) + g0, short(0), grec, kBufferWord3);
-        pg = make_float2(__uint_as_float(ld(ra, (lane % CT) * ht)),
-                         __uint_as_float(ld(rb, (lane % CT) * ht)));
+        // gates of token k CT + lane % CT, for the ratios
+        if (pw == 0)
+            pg = load_gates(k);
     };
 
-    // conv + SiLU, norm factors and coefficients of chunk k into ys[k & 1],
-    // sc[k % 3], alf[k % 3] and nofold[k % 3], for the wave's tokens
-    // [t0, t0 + TPW).  The 2 TPW wave sums (|q|^2, |k|^2 of each token) are
-    // reduced together, and lane i finishes the coefficients of the wave's
-    // i-th token.
+    // conv + SiLU of chunk k for the wave's tokens [t0, t0 + TPW): v into
+    // vt[k % 3] (transposed), the bf16 halves of q^ and k^ into qr / kr[k % 3]
+    // (and of k^ by key into kc[k % 3]) once the wave has reduced the 2 TPW
+    // sums |q|^2, |k|^2 of its tokens.  Every token is
+    // computed, also past the sequence's end.  Wave 0 also writes the gates
+    // and the decay ratios r(t, s) into gt / rt[k & 1].
     auto prepare = [&](int k) {
         static_assert(TPW == 4, "the sums of 4 tokens are reduced together");
         if (k >= nchunks)
             return;
-        const int buf = k & 1, sb = k % 3;
-        const int nt = chunk_len(k);
-        // v: one (token, pair) job per lane
+        const int b3 = k % 3;
+        // the conv sums first: once they have read the raw rows, the next
+        // chunk's loads go out (into the same registers) and have the rest of
+        // this stage, besides the interval's wait, to arrive
+        const float2 pk = pg; // this chunk's gates (the loads below overwrite pg)
+        float2 va[NVJ];
 #pragma unroll
         for (int jj = 0; jj < NVJ; ++jj) {
-            const int tt = t0 + vi[jj];
-            if (vi[jj] < TPW && tt < nt) {
-                float a0 = bv[jj][0], a1 = bv[jj][1];
+            float a0 = bv[jj].x, a1 = bv[jj].y;
 #pragma unroll
-                for (int w = 0; w < W; ++w) {
-                    a0 = fmaf(wv[jj][0][w], lo_bf16(xv[jj][w]), a0);
-                    a1 = fmaf(wv[jj][1][w], hi_bf16(xv[jj][w]), a1);
-                }
-                *reinterpret_cast<float2*>(&ys[buf][tt][2 * DK + 2 * vpj[jj]]) =
-                    make_float2(silu(a0), silu(a1));
+            for (int w = 0; w < W; ++w) {
+                const float2 tw = taps[w][2 * QKP + vpj[jj]];
+                a0 = fmaf(tw.x, lo_bf16(xv[jj][w]), a0);
+                a1 = fmaf(tw.y, hi_bf16(xv[jj][w]), a1);
             }
+            va[jj] = make_float2(a0, a1);
         }
         // q, k: the lane walks the wave's tokens over its register rows
-        auto conv1 = [&](const float (&wt)[W], float b, const uint32_t (&xr)[NR], int i, bool hi) {
-            float acc = b;
+        float2 tq[W], tk[W];
 #pragma unroll
-            for (int w = 0; w < W; ++w)
-                acc = fmaf(wt[w], hi ? hi_bf16(xr[i + w]) : lo_bf16(xr[i + w]), acc);
-            return silu(acc);
+        for (int w = 0; w < W; ++w) {
+            tq[w] = taps[w][qkp];
+            tk[w] = taps[w][QKP + qkp];
+        }
+        auto conv2 = [&](const float2 (&tw)[W], float2 b, const uint32_t (&xr)[NR], int i) {
+            float a0 = b.x, a1 = b.y;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                a0 = fmaf(tw[w].x, lo_bf16(xr[i + w]), a0);
+                a1 = fmaf(tw[w].y, hi_bf16(xr[i + w]), a1);
+            }
+            return make_float2(a0, a1);
         };
-        float sq[TPW], sk[TPW];
+        float2 qv[TPW], kv[TPW];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-            sq[i] = sk[i] = 0.f;
-            const int tt = t0 + i;
-            if (tt >= nt)
-                break;
-            const float q0 = conv1(wq[0], bq[0], xq, i, false);
-            const float q1 = conv1(wq[1], bq[1], xq, i, true);
-            const float k0 = conv1(wk[0], bk[0], xk, i, false);
-            const float k1 = conv1(wk[1], bk[1], xk, i, true);
-            if (lane < QKP) {
-                *reinterpret_cast<float2*>(&ys[buf][tt][2 * lane]) = make_float2(q0, q1);
-                *reinterpret_cast<float2*>(&ys[buf][tt][DK + 2 * lane]) = make_float2(k0, k1);
-                sq[i] = fmaf(q0, q0, q1 * q1);
-                sk[i] = fmaf(k0, k0, k1 * k1);
+            qv[i] = conv2(tq, bq, xq, i);
+            kv[i] = conv2(tk, bk, xk, i);
+        }
+        issue(k + 1);
+#pragma unroll
+        for (int jj = 0; jj < NVJ; ++jj) {
+            if (vi[jj] < TPW) {
+                const int tt = t0 + vi[jj];
+                vt[b3][2 * vpj[jj]][tt] = silu(va[jj].x);
+                vt[b3][2 * vpj[jj] + 1][tt] = silu(va[jj].y);
             }
+        }
+        float sq[TPW], sk[TPW];
+        const bool own = lane < QKP;
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            qv[i] = make_float2(silu(qv[i].x), silu(qv[i].y));
+            kv[i] = make_float2(silu(kv[i].x), silu(kv[i].y));
+            sq[i] = own ? fmaf(qv[i].x, qv[i].x, qv[i].y * qv[i].y) : 0.f;
+            sk[i] = own ? fmaf(kv[i].x, kv[i].x, kv[i].y * kv[i].y) : 0.f;
         }
         // wave sums: halves (tokens 0|1 and 2|3 share a register), then rows
         // (row j then holds token (0, 2, 1, 3)[j]), then within the rows
@@ -601,153 +819,49 @@ void prefill_kernel(PrefillParams p)
             return group_sum<16>(fold_rows(fold_halves(v[0], v[1]), fold_halves(v[2], v[3])));
         };
         const float tsq = token_sums(sq), tsk = token_sums(sk);
-        const int src = 16 * (((lane & 1) << 1) | ((lane >> 1) & 1)); // row of token lane & 3
-        const float my_sq = __shfl(tsq, src, 64), my_sk = __shfl(tsk, src, 64);
-        // running products of the chunk's decays: an inclusive scan over each
-        // 16-lane row (lane i of a row: token i; lanes past the chunk's end
-        // take 1).  Whether the state's scale can stay unfolded through the
-        // chunk: every decay in [0, 1] and their product at least 2^-40, so
-        // that no running product falls below it (NaN fails the test).
-        const int ti = lane % CT;
-        const float av = ti < nt ? pg.x : 1.f;
-        float cp = av;
-        cp *= row_shr_or_one<1>(cp);
-        cp *= row_shr_or_one<2>(cp);
-        cp *= row_shr_or_one<4>(cp);
-        cp *= row_shr_or_one<8>(cp);
-        if (pw == 0) {
-            const bool ok = av >= 0.f && av <= 1.f;
-            const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cp), 15));
-            const bool quiet = __ballot(!ok) == 0 && total >= __uint_as_float(kFoldBelow);
-            if (lane == 0)
-                nofold[sb] = quiet ? 1u : 0u;
-        }
-        const int tt = t0 + (lane & 3);
-        const float ct = __shfl(cp, tt, 64); // running product through token tt
-        const float ga = __shfl(pg.x, tt, 64), gb = __shfl(pg.y, tt, 64);
-        if (lane < TPW && tt < nt) {
-            const float rq = p.scale * __builtin_amdgcn_rsqf(my_sq + p.eps);
-            const float rk = __builtin_amdgcn_rsqf(my_sk + p.eps);
-            float* o = sc[sb][tt];
-            *reinterpret_cast<float4*>(o + SC_SCALED) =
-                make_float4(ct * rk, gb, rk * __builtin_amdgcn_rcpf(ct), ct);
-            *reinterpret_cast<float4*>(o + SC_PLAIN) = make_float4(ga, gb, rk, rq);
-            alf[k % 3][tt] = ct * rq;
-        }
-    };
-
-    // Output products of chunk k, while the consumers run it: producer wave
-    // j < NCB forms S_0 Q^T for the slice's j-th 16-column block (to LDS for
-    // the epilogue), the others form the GP parts of Q K^T over
-    // slices of the key range (to LDS; a single part goes to wave 0 when no
-    // wave is free).  MFMA lane l supplies A[l % 16][l / 16] and
-    // B[l / 16][l % 16] and receives D[4 (l / 16) + r][l % 16] in r; the K
-    // index of a step is permuted so that lane group l / 16 reads one run of
-    // consecutive keys.
-    constexpr int GP = Sh::GP;
-    const int m16 = lane % 16, q4 = lane / 16;
-    auto product = [&](const float* arow, const float* brow, int ngroups) {
-        // four independent accumulation chains keep the matrix pipe busy
-        v4f ac[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
-                     {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        // row j of the sums holds token (0, 2, 1, 3)[j]; lane i < 4 takes token i's
+        const int src = 16 * (((lane & 1) << 1) | ((lane >> 1) & 1));
+        const float rq = p.scale * __builtin_amdgcn_rsqf(__shfl(tsq, src, 64) + p.eps);
+        const float rk = __builtin_amdgcn_rsqf(__shfl(tsk, src, 64) + p.eps);
+        if (own) {
+            // the lane's keys 2 lane and 2 lane + 1 sit side by side in a row
+            const int kp = key_pos<Sh::X32>(2 * lane);
+            uint16_t kch[2][TPW], kcl[2][TPW];
 #pragma unroll
-        for (int i = 0; i < ngroups; ++i) {
-            const float4 a = *reinterpret_cast<const float4*>(arow + 4 * i);
-            const float4 b = *reinterpret_cast<const float4*>(brow + 4 * i);
-            ac[0] = mfma16(a.x, b.x, ac[0]);
-            ac[1] = mfma16(a.y, b.y, ac[1]);
-            ac[2] = mfma16(a.z, b.z, ac[2]);
-            ac[3] = mfma16(a.w, b.w, ac[3]);
-        }
-        return (ac[0] + ac[1]) + (ac[2] + ac[3]);
-    };
-    auto products = [&](int k) {
-        const int buf = k & 1;
-        if (pw < NCB) // S_0[col][key] x Q[t][key], for the block's epilogue
-            pq[buf][pw][lane] = product(&s0[16 * pw + m16][q4 * KQ], &ys[buf][m16][q4 * KQ], KQ / 4);
-        const int gpart = Sh::GFREE > 0 ? pw - NCB : (pw == 0 ? 0 : -1);
-        if (gpart >= 0 && gpart < GP) { // Q[t][key] x K[s][key] over a slice of the keys
-            constexpr int NG = KQ / 4 / GP;
-            const int k0 = q4 * KQ + 4 * NG * gpart;
-            const v4f g4 = product(&ys[buf][m16][k0], &ys[buf][m16][DK + k0], NG);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                gq[buf][gpart][4 * q4 + r][m16] = g4[r];
-        }
-    };
-
-    // Outputs of chunk k (after it): o = alf_t (S_0 Q^T) + D M^T for the
-    // wave's column block, written as bf16 (a lane: 4 columns of token l % 16).
-    // M[t][s] = (A_t / A_s) rq_t rk_s (q_t . k_s) for s <= t, else 0; chunks
-    // without a fold take A_t rq_t (alf) and rk_s / A_s (SC_SCALED), the
-    // others multiply the decays between s and t one by one.  A lane builds
-    // the B operand it supplies, M[t = l % 16][s = 4 (l / 16) + j], j = 0..3.
-    auto epilogue = [&](int k) {
-        // block eb of the chunk; on the waves without a block when there are
-        // enough of them (they carry the lighter products), else the block's own
-        const int eb = Sh::GFREE >= NCB ? pw - (Sh::NPROD - NCB) : pw;
-        if (eb < 0 || eb >= NCB)
-            return;
-        const int buf = k & 1, sb = k % 3;
-        const int t_ = m16;
-        float4 gsum = *reinterpret_cast<const float4*>(&gq[buf][0][t_][4 * q4]);
-#pragma unroll
-        for (int j = 1; j < GP; ++j) {
-            const float4 e = *reinterpret_cast<const float4*>(&gq[buf][j][t_][4 * q4]);
-            gsum.x += e.x;
-            gsum.y += e.y;
-            gsum.z += e.z;
-            gsum.w += e.w;
-        }
-        const float gs[4] = {gsum.x, gsum.y, gsum.z, gsum.w};
-        const float at = alf[k % 3][t_];
-        const bool quiet = __builtin_amdgcn_readfirstlane(nofold[sb]) != 0u;
-        float f[4];
-        if (quiet) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                f[j] = at * sc[sb][4 * q4 + j][SC_SCALED + 2];
-        } else {
-            // the decays between s and t, one token at a time (rare)
-            f[0] = f[1] = f[2] = f[3] = 1.f;
-#pragma unroll 1
-            for (int u = 1; u < CT; ++u) {
-                const float au = sc[sb][u][SC_PLAIN];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    f[j] *= (u > 4 * q4 + j && u <= t_) ? au : 1.f;
+            for (int i = 0; i < TPW; ++i) {
+                const float fq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rq), i));
+                const float fk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rk), i));
+                uint16_t h0, l0, h1, l1;
+                split_bf16(qv[i].x * fq, h0, l0);
+                split_bf16(qv[i].y * fq, h1, l1);
+                *reinterpret_cast<uint32_t*>(&qr[b3][0][t0 + i][kp]) = h0 | (uint32_t(h1) << 16);
+                *reinterpret_cast<uint32_t*>(&qr[b3][1][t0 + i][kp]) = l0 | (uint32_t(l1) << 16);
+                split_bf16(kv[i].x * fk, kch[0][i], kcl[0][i]);
+                split_bf16(kv[i].y * fk, kch[1][i], kcl[1][i]);
+                *reinterpret_cast<uint32_t*>(&kr[b3][0][t0 + i][kp]) = kch[0][i] | (uint32_t(kch[1][i]) << 16);
+                *reinterpret_cast<uint32_t*>(&kr[b3][1][t0 + i][kp]) = kcl[0][i] | (uint32_t(kcl[1][i]) << 16);
             }
-            const float rq = sc[sb][t_][SC_PLAIN + 3];
+            // k^ columns of the two keys over the wave's 4 tokens (one 8-byte store each)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                f[j] *= rq * sc[sb][4 * q4 + j][SC_PLAIN + 2];
+            for (int e = 0; e < 2; ++e) {
+                *reinterpret_cast<uint2*>(&kc[b3][0][2 * lane + e][t0]) =
+                    make_uint2(kch[e][0] | (uint32_t(kch[e][1]) << 16), kch[e][2] | (uint32_t(kch[e][3]) << 16));
+                *reinterpret_cast<uint2*>(&kc[b3][1][2 * lane + e][t0]) =
+                    make_uint2(kcl[e][0] | (uint32_t(kcl[e][1]) << 16), kcl[e][2] | (uint32_t(kcl[e][3]) << 16));
+            }
         }
-        v4f acc = pq[buf][eb][lane] * at;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int s_ = 4 * q4 + j;
-            acc = mfma16(dbuf[buf][s_][16 * eb + m16], s_ <= t_ ? gs[j] * f[j] : 0.f, acc);
-        }
-        if (m16 < chunk_len(k)) {
-            *reinterpret_cast<uint2*>(out_base + int64_t(k * CT + m16) * out_tok + 16 * eb + 4 * q4) =
-                pack_bf16x4(acc[0], acc[1], acc[2], acc[3]);
-        }
+        if (pw == 0)
+            write_ratios(k, pk);
     };
 
     issue(0);
-    prepare(0);
-    issue(1);
-    __syncthreads(); // B
-    for (int c = 0; c < nchunks; ++c) {
-        __syncthreads(); // X: the consumers have written the chunk's starting state
-        if (c >= 1)
-            epilogue(c - 1);
-        products(c);
-        prepare(c + 1);
-        issue(c + 2);
-        __syncthreads(); // P
+    __syncthreads(); // taps in LDS
+    for (int c = 0; c < nchunks + 2; ++c) {
+        prepare(c); // also issues chunk c + 1's loads
+        if (c >= 1 && (!Sh::NFIN || pw >= 1))
+            finish(c - 1, pw);
+        __syncthreads(); // end of interval c
     }
-    epilogue(nchunks - 1);
 }
 
 // Final window of each sequence: the last W-1 entries of (old window, x).
@@ -818,12 +932,12 @@ __global__ __launch_bounds__(kWinThreads) void prefill_window_kernel(WindowParam
     }
 }
 
-template <int DK, int DV, int W>
+template <int DK, int DV, int W, int SWR>
 int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, int64_t total_tokens,
                      const int32_t* cu, const gdn_step_args* a, const int32_t* ckpt_slot,
                      const int32_t* ckpt_len, hipStream_t stream)
 {
-    using Sh = PrefillShape<DK, DV>;
+    using Sh = PrefillShape<DK, DV, SWR>;
     const gdn_pool_desc& d = pool->desc;
     PrefillParams p;
     p.layer = static_cast<uint8_t*>(pool->bases[layer]);
@@ -852,7 +966,7 @@ int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, int6
     const int64_t blocks = int64_t(num_seqs) * d.num_v_heads * Sh::NSL;
     if (blocks > INT32_MAX)
         return fail(GDN_ERANGE, "prefill grid too large");
-    hipLaunchKernelGGL((prefill_kernel<DK, DV, W>), dim3(uint32_t(blocks)), dim3(Sh::NT), 0,
+    hipLaunchKernelGGL((prefill_kernel<DK, DV, W, SWR>), dim3(uint32_t(blocks)), dim3(Sh::NT), 0,
                        stream, p);
     int rc = check_launch("prefill");
     if (rc != GDN_OK)
@@ -880,16 +994,51 @@ int launch_prefill_t(const gdn_pool* pool, int32_t layer, int32_t num_seqs, int6
     return check_launch("prefill window");
 }
 
-template <int DK>
+// Compute units of the calling thread's current device (looked up once per device).
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (dev < 64)
+        cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+template <int DK, int SWR>
 int dispatch_w(const gdn_pool* pool, int32_t layer, int32_t num_seqs, int64_t T, const int32_t* cu,
                const gdn_step_args* a, const int32_t* cs, const int32_t* cl, hipStream_t stream)
 {
     switch (pool->desc.conv_width) {
-    case 2: return launch_prefill_t<DK, DK, 2>(pool, layer, num_seqs, T, cu, a, cs, cl, stream);
-    case 3: return launch_prefill_t<DK, DK, 3>(pool, layer, num_seqs, T, cu, a, cs, cl, stream);
-    case 4: return launch_prefill_t<DK, DK, 4>(pool, layer, num_seqs, T, cu, a, cs, cl, stream);
+    case 2: return launch_prefill_t<DK, DK, 2, SWR>(pool, layer, num_seqs, T, cu, a, cs, cl, stream);
+    case 3: return launch_prefill_t<DK, DK, 3, SWR>(pool, layer, num_seqs, T, cu, a, cs, cl, stream);
+    case 4: return launch_prefill_t<DK, DK, 4, SWR>(pool, layer, num_seqs, T, cu, a, cs, cl, stream);
     default: return fail(GDN_EUNSUPPORTED, "prefill: conv width %d", pool->desc.conv_width);
     }
+}
+
+// Head size 128: 64-column workgroups while they all fit on the GPU at once
+// (the critical path is then the longest sequence, which gets twice the CUs),
+// whole-head workgroups when the batch needs several rounds of them.
+int dispatch_128(const gdn_pool* pool, int32_t layer, int32_t num_seqs, int64_t T,
+                 const int32_t* cu, const gdn_step_args* a, const int32_t* cs, const int32_t* cl,
+                 hipStream_t stream)
+{
+    const int cus = device_cus();
+    if (cus <= 0)
+        return fail(GDN_EHIP, "cannot query the device's compute units");
+    if (int64_t(num_seqs) * pool->desc.num_v_heads * 2 <= cus)
+        return dispatch_w<128, 4>(pool, layer, num_seqs, T, cu, a, cs, cl, stream);
+    return dispatch_w<128, 8>(pool, layer, num_seqs, T, cu, a, cs, cl, stream);
 }
 
 } // namespace
@@ -905,10 +1054,10 @@ int launch_prefill(const gdn_pool* pool, int32_t layer, int32_t num_seqs, int64_
 {
     const int32_t *cs = ckpt_slot, *cl = ckpt_len;
     switch (pool->desc.head_k_dim) {
-    case 16: return dispatch_w<16>(pool, layer, num_seqs, total_tokens, cu, a, cs, cl, stream);
-    case 32: return dispatch_w<32>(pool, layer, num_seqs, total_tokens, cu, a, cs, cl, stream);
-    case 64: return dispatch_w<64>(pool, layer, num_seqs, total_tokens, cu, a, cs, cl, stream);
-    case 128: return dispatch_w<128>(pool, layer, num_seqs, total_tokens, cu, a, cs, cl, stream);
+    case 16: return dispatch_w<16, 4>(pool, layer, num_seqs, total_tokens, cu, a, cs, cl, stream);
+    case 32: return dispatch_w<32, 4>(pool, layer, num_seqs, total_tokens, cu, a, cs, cl, stream);
+    case 64: return dispatch_w<64, 4>(pool, layer, num_seqs, total_tokens, cu, a, cs, cl, stream);
+    case 128: return dispatch_128(pool, layer, num_seqs, total_tokens, cu, a, cs, cl, stream);
     default: return fail(GDN_EUNSUPPORTED, "prefill: head dim %d", pool->desc.head_k_dim);
     }
 }

@@ -26,15 +26,15 @@ INT32_MAX = 2**31 - 1
 OUT_OF_RANGE = 0xFFFFFFF0
 
 
-def shape(dk):
-    kpl = 16 if dk >= 128 else (8 if dk >= 32 else 4)
-    lpc = dk // kpl
-    cpw = 64 // lpc
-    ncons = min(dk // cpw, 4)
-    isz = ncons * cpw
+def shape(dk, swr=4):
+    """Column slice of a workgroup: up to `swr` 16-column blocks of the head
+    (4, or 8 for whole 128-column heads)."""
+    nb = dk // 16
+    sw = min(nb, swr)
+    isz = 16 * sw
     tpw = CT // NPROD
     nvp = isz // 2
-    return dict(ISZ=isz, NSL=dk // isz, TPW=tpw, QKP=dk // 2, NVP=nvp,
+    return dict(ISZ=isz, NSL=nb // sw, TPW=tpw, QKP=dk // 2, NVP=nvp,
                 NVJ=(tpw * nvp + 63) // 64)
 
 
@@ -42,9 +42,9 @@ def range_bytes(n):
     return min(n, INT32_MAX)
 
 
-def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows):
+def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows, swr=4):
     """All producer loads of all workgroups of one sequence."""
-    sh = shape(dk)
+    sh = shape(dk, swr)
     C = 2 * Hk * dk + Hv * dk
     rowb = 2 * C
     HR, TPW = W - 1, sh["TPW"]
@@ -165,6 +165,18 @@ def test_producer_loads_workload_lengths(W):
     tb = 0
     for i, L in enumerate(lengths):
         check_sequence(128, W, 2, 4, L, tb, warm=i < 4, total_rows=total)
+        tb += L
+
+
+@pytest.mark.parametrize("W", [2, 4])
+def test_producer_loads_whole_head_workgroups(W):
+    # head size 128 in whole-head workgroups (64 sequences x 1000 tokens
+    # at 32 v-heads uses them); ragged lengths and the 1000-token rows
+    lengths = list(range(1, 40)) + [1000, 1000]
+    total = sum(lengths)
+    tb = 0
+    for i, L in enumerate(lengths):
+        check_sequence(128, W, 2, 4, L, tb, warm=bool(i % 2), total_rows=total, swr=8)
         tb += L
 
 

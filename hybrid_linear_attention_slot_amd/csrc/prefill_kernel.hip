@@ -50,11 +50,12 @@
 //   - four conv waves prepare the chunks: raw inputs loaded into registers a
 //     chunk ahead, conv + SiLU, the L2-normalised q^ and k^ rows and v (per
 //     chunk c); one chunk later the chunk's Gram products k^ k^T and q^ k^T,
-//     L, its inverse T, the output mask M and the decay products are formed:
-//     in a 64-column workgroup a fifth wave forms L and T (so that no wave
-//     carries both the conv and the inversion) and conv waves 1 and 2 form M
-//     and the decay products; in a whole-head one conv waves 0-2 share all
-//     three.  Conv wave 0 also writes each chunk's gates and decay ratios.
+//     L, its inverse T, the output mask M (as two key halves) and the decay
+//     products are formed: in a 64-column workgroup a fifth wave forms L and
+//     T (so that no wave carries both the conv and the inversion) and conv
+//     waves 1-3 the halves of M and the decay products; in a whole-head one
+//     conv waves 0-3 share all four parts.  Conv wave 0 also writes each
+//     chunk's gates and decay ratios.
 // A chunk is prepared in interval c (conv), finished in c + 1 (T, M, decays)
 // and consumed by the state waves in c + 2; one barrier ends each interval,
 // so q^/k^/v rows are triple-buffered and T, M and the coefficients double-
@@ -180,7 +181,8 @@ constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer resource, gfx9-fam
 // over distinct resources.
 __device__ __forceinline__ int range_bytes(int64_t n)
 {
-    const int r = n > int64_t(INT32_MAX) ? INT32_MAX : int(n);
+    // clamped at 0: a negative range would turn the range check off
+    const int r = n > int64_t(INT32_MAX) ? INT32_MAX : (n < 0 ? 0 : int(n));
     return __builtin_amdgcn_readfirstlane(r);
 }
 
@@ -288,7 +290,9 @@ void prefill_kernel(PrefillParams p)
     __shared__ __align__(16) float gt[2][2][CT];    // decay (1 past the end), beta (0 past it)
     __shared__ __align__(16) float rt[2][CT][TS];   // r(t, s) for s < t, 1 for s >= t
     __shared__ __align__(16) float tm[2][CT][TS];   // T = (I + L)^-1
-    __shared__ __align__(16) float mm[2][CT][TS];   // M[t][s] = r(t, s) q^_t . k^_s (s <= t)
+    // M[t][s] = r(t, s) q^_t . k^_s (s <= t), as two terms: the Gram products
+    // over the first and the second half of the keys
+    __shared__ __align__(16) float mm[2][2][CT][TS];
     __shared__ __align__(16) float cf[2][CF_N][CT]; // CF_* rows
     __shared__ __align__(16) float lw[CT][TS];      // L of the chunk being inverted
     // conv taps of the slice's channel pairs, [tap][q pairs | k pairs | v pairs]
@@ -358,12 +362,13 @@ void prefill_kernel(PrefillParams p)
         return 2 * p.Hk * DK + h * DV + sl * ISZ + (ch - 2 * DK);
     };
 
-    // Gates of token k CT + lane % CT of head h (zero past the sequence's end):
-    // buffer loads whose range check covers the sequence's tokens only.
-    auto load_gates = [&](int k) {
+    // Gates of token k CT + lane % CT of head h (zero past the sequence's end,
+    // and everywhere when `use` is false): buffer loads whose range check
+    // covers the sequence's tokens only.
+    auto load_gates = [&](int k, bool use) {
         const int ht = p.Hv * 4;
         const int64_t g0 = int64_t(tb + k * CT) * p.Hv + h;
-        const int grec = range_bytes(int64_t(L - k * CT) * ht);
+        const int grec = use ? range_bytes(int64_t(L - k * CT) * ht) : 0;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float*>(p.alpha) + g0, short(0), grec, kBufferWord3);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
@@ -399,24 +404,37 @@ void prefill_kernel(PrefillParams p)
     };
 
     // Chunk k's T, M and coefficients (interval k + 1), from its rows, gates
-    // and decay ratios, in three parts: (0) L from the Gram matrix k^ k^T and
-    // T = (I + L)^-1 by forward substitution, (1) M from q^ k^T, (2) the decay
-    // products.  Part 0 writes and reads back lw within one wave.
+    // and decay ratios, in four parts: (0) L from the Gram matrix k^ k^T and
+    // T = (I + L)^-1 by forward substitution, (1) and (3) the two key halves
+    // of M from q^ k^T, (2) the decay products.  Part 0 writes and reads back
+    // lw within one wave.
+    // the lane's element (t, s) = (4 q4, m16) of a 16 x TS tile, in floats;
+    // opaque, so that the loop reads it from a register instead of forming it
+    // again with a multiply whose (unused) high half can alias a register
+    // that a load is still writing, which would make the read wait
+    int tile_lane = 4 * q4 * TS + m16;
+    asm volatile("" : "+v"(tile_lane));
     auto finish = [&](int k, int part) {
-        if (k >= nchunks || part >= 3)
+        if (k >= nchunks || part >= 4)
             return;
         const int b3 = k % 3, b2 = k & 1;
+        // r(4 q4 + r, m16) at rtl[r TS]: every lane reads, the mask is applied after
+        const float* rtl = &rt[b2][0][0] + tile_lane;
         const int pw = part;
-        if (pw <= 1) {
-            // Gram: G[t][s] = x_t . k^_s, x = k^ (wave 0) or q^ (wave 1);
-            // register r: t = 4 q4 + r, s = m16 (rows are A and B operands
-            // alike: lane l reads row l % 16)
+        if (pw != 2) {
+            // Gram: G[t][s] = x_t . k^_s, x = k^ (part 0) or q^ (parts 1, 3:
+            // MFMA steps [0, NKH) and [NKH, NKC)); register r: t = 4 q4 + r,
+            // s = m16 (rows are A and B operands alike: lane l reads row l % 16)
             const uint16_t(*xh)[KS] = pw == 0 ? kr[b3][0] : qr[b3][0];
             const uint16_t(*xl)[KS] = pw == 0 ? kr[b3][1] : qr[b3][1];
+            constexpr int NKH = Sh::NKC >= 2 ? Sh::NKC / 2 : Sh::NKC;
+            const int c2b = pw == 3 ? NKH : 0, c2e = pw == 1 ? NKH : Sh::NKC;
             v4f gm = {0.f, 0.f, 0.f, 0.f};
             if constexpr (Sh::X32) {
 #pragma unroll
                 for (int c2 = 0; c2 < Sh::NKC; ++c2) {
+                    if (c2 < c2b || c2 >= c2e)
+                        continue;
                     const int kp = 32 * c2 + 8 * q4;
                     auto ld8 = [&](const uint16_t* row) {
                         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + kp));
@@ -428,14 +446,18 @@ void prefill_kernel(PrefillParams p)
                 auto ld4 = [&](const uint16_t* row) {
                     return __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(row + 4 * q4));
                 };
-                gm = mfma3_k16(ld4(xh[m16]), ld4(xl[m16]), ld4(kr[b3][0][m16]), ld4(kr[b3][1][m16]), gm);
+                if (pw != 3) // one step: all of it in parts 0 and 1
+                    gm = mfma3_k16(ld4(xh[m16]), ld4(xl[m16]), ld4(kr[b3][0][m16]), ld4(kr[b3][1][m16]), gm);
             }
             const int s_ = m16;
             if (pw == 0) {
+                const float4 bt = *reinterpret_cast<const float4*>(&gt[b2][1][4 * q4]);
+                const float bts[4] = {bt.x, bt.y, bt.z, bt.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t_ = 4 * q4 + r;
-                    lw[t_][s_] = s_ < t_ ? gt[b2][1][t_] * rt[b2][t_][s_] * gm[r] : 0.f;
+                    const float l = bts[r] * rtl[r * TS] * gm[r];
+                    (&lw[0][0])[tile_lane + r * TS] = s_ < t_ ? l : 0.f;
                 }
                 // the wave's own LDS writes above are read back by other lanes
                 lds_wave_sync();
@@ -464,7 +486,8 @@ void prefill_kernel(PrefillParams p)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t_ = 4 * q4 + r;
-                    mm[b2][t_][s_] = s_ <= t_ ? rt[b2][t_][s_] * gm[r] : 0.f;
+                    const float mv = rtl[r * TS] * gm[r];
+                    (&mm[b2][pw == 3][0][0])[tile_lane + r * TS] = s_ <= t_ ? mv : 0.f;
                 }
             }
         } else if (lane < CT) {
@@ -575,7 +598,9 @@ void prefill_kernel(PrefillParams p)
                 d = mfma16(tt.z, R2, d);
                 d = mfma16(tt.w, R3, d);
                 // outputs: O^T = A_t O^T + D^T M^T (lane: 4 columns of token m16)
-                const float4 mv = *reinterpret_cast<const float4*>(&mm[b2][m16][4 * q4]);
+                const float4 m0 = *reinterpret_cast<const float4*>(&mm[b2][0][m16][4 * q4]);
+                const float4 m1 = *reinterpret_cast<const float4*>(&mm[b2][1][m16][4 * q4]);
+                const float4 mv = make_float4(m0.x + m1.x, m0.y + m1.y, m0.z + m1.z, m0.w + m1.w);
                 O *= cf[b2][CF_A][m16];
                 O = mfma16(d[0], mv.x, O);
                 O = mfma16(d[1], mv.y, O);
@@ -689,28 +714,38 @@ void prefill_kernel(PrefillParams p)
     auto ld = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0);
     };
-    auto issue = [&](int k) {
-        if (k >= nchunks)
-            return;
-        const int rbase = k * CT + t0 - HR; // the wave's first row
-        // the first of its rows inside the sequence; L (an empty range) when
-        // the wave's tokens all lie past the end of a short last chunk
-        const int xb = min(max(rbase, 0), L);
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(p.x) + int64_t(tb + xb) * p.C, short(0),
-            range_bytes(int64_t(L - xb) * rowb), kBufferWord3);
+    // The in-loop form has no branch and no early return: a load skipped on
+    // one path would make the compiler merge the two paths' registers with
+    // copies, and a copy of a register still being loaded waits for the load.
+    // Past the sequence's end the ranges are empty (the loads return zero).
+    auto rows_resource = [&](int xb) { // rows from xb on (xb <= L)
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x) + int64_t(tb + xb) * p.C,
+                                                 short(0), range_bytes(int64_t(L - xb) * rowb),
+                                                 kBufferWord3);
+    };
+    auto load_rows = [&](__amdgpu_buffer_rsrc_t rs) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            xq[i] = ld(rs, oq + i * rowb);
+            xk[i] = ld(rs, ok + i * rowb);
+        }
+#pragma unroll
+        for (int jj = 0; jj < NVJ; ++jj)
+#pragma unroll
+            for (int w = 0; w < W; ++w)
+                xv[jj][w] = ld(rs, ov[jj] + w * rowb);
+    };
+    // chunk k >= 1: the wave's first row k CT + t0 - HR is not before the
+    // sequence's start (L, an empty range, once past its end)
+    auto issue = [&](int k) { load_rows(rows_resource(min(k * CT + t0 - HR, L))); };
+    // chunk 0: wave 0's first rows come from the window
+    auto issue_first = [&]() {
+        const int rbase = t0 - HR;
+        pg = load_gates(0, pw == 0);
         if (rbase >= 0) {
-#pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                xq[i] = ld(rs, oq + i * rowb);
-                xk[i] = ld(rs, ok + i * rowb);
-            }
-#pragma unroll
-            for (int jj = 0; jj < NVJ; ++jj)
-#pragma unroll
-                for (int w = 0; w < W; ++w)
-                    xv[jj][w] = ld(rs, ov[jj] + w * rowb);
+            issue(0);
         } else {
+            const __amdgpu_buffer_rsrc_t rs = rows_resource(0);
             // the first chunk of wave 0: rows -HR .. -1 come from the window
             const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t*>(win), short(0), warm ? HR * rowb : 0, kBufferWord3);
@@ -731,9 +766,6 @@ void prefill_kernel(PrefillParams p)
                 }
             }
         }
-        // gates of token k CT + lane % CT, for the ratios
-        if (pw == 0)
-            pg = load_gates(k);
     };
 
     // conv + SiLU of chunk k for the wave's tokens [t0, t0 + TPW): v into
@@ -742,15 +774,12 @@ void prefill_kernel(PrefillParams p)
     // sums |q|^2, |k|^2 of its tokens.  Every token is
     // computed, also past the sequence's end.  Wave 0 also writes the gates
     // and the decay ratios r(t, s) into gt / rt[k & 1].
-    auto prepare = [&](int k) {
+    auto prepare = [&](int k) { // k < nchunks
         static_assert(TPW == 4, "the sums of 4 tokens are reduced together");
-        if (k >= nchunks)
-            return;
         const int b3 = k % 3;
         // the conv sums first: once they have read the raw rows, the next
         // chunk's loads go out (into the same registers) and have the rest of
-        // this stage, besides the interval's wait, to arrive
-        const float2 pk = pg; // this chunk's gates (the loads below overwrite pg)
+        // the interval and the next one's start to arrive
         float2 va[NVJ];
 #pragma unroll
         for (int jj = 0; jj < NVJ; ++jj) {
@@ -785,6 +814,10 @@ void prefill_kernel(PrefillParams p)
             qv[i] = conv2(tq, bq, xq, i);
             kv[i] = conv2(tk, bk, xk, i);
         }
+        // keep the loads below the sums: loads moved above them would need
+        // registers of their own, and the copies into the loop's registers
+        // would wait for the loads at the interval's end
+        __builtin_amdgcn_sched_barrier(0);
         issue(k + 1);
 #pragma unroll
         for (int jj = 0; jj < NVJ; ++jj) {
@@ -851,17 +884,25 @@ void prefill_kernel(PrefillParams p)
             }
         }
         if (pw == 0)
-            write_ratios(k, pk);
+            write_ratios(k, pg);
+        pg = load_gates(k + 1, pw == 0); // after its last use, for the same reason
     };
 
-    issue(0);
+    issue_first();
     __syncthreads(); // taps in LDS
-    for (int c = 0; c < nchunks + 2; ++c) {
+    const bool fin = !Sh::NFIN || pw >= 1; // a finish part of its own
+    for (int c = 0; c < nchunks; ++c) {
         prepare(c); // also issues chunk c + 1's loads
-        if (c >= 1 && (!Sh::NFIN || pw >= 1))
-            finish(c - 1, pw);
+        if (c >= 1 && fin)
+            finish(c - 1, pw); // part pw of the previous chunk
         __syncthreads(); // end of interval c
     }
+    // intervals nchunks and nchunks + 1: the last chunk's finish parts, then
+    // the state waves' last chunk
+    if (fin)
+        finish(nchunks - 1, pw);
+    __syncthreads();
+    __syncthreads();
 }
 
 // Final window of each sequence: the last W-1 entries of (old window, x).

@@ -13,10 +13,15 @@ over ragged lengths, and checks:
     wave owns, and at the row its token needs (so no needed row is refused);
   * window loads stay inside the window region, and the window resource is
     empty when the sequence starts cold (a cold page is never read);
-  * gate loads stay inside the sequence's tokens.
+  * gate loads stay inside the sequence's tokens, and the waves that do not
+    use the gates load none.
 
-The arithmetic is restated from the kernel's `issue` (prefill_kernel.hip);
-a change there must be mirrored here before the kernel runs on a GPU.
+The loop issues the loads of chunk c + 1 while it prepares chunk c, with no
+branch, so it also loads a chunk past the last one (c = nchunks - 1); those
+rows lie past the sequence's end, where the ranges are empty.  The
+arithmetic is restated from the kernel's `issue` / `issue_first`
+(prefill_kernel.hip); a change there must be mirrored here before the
+kernel runs on a GPU.
 """
 import numpy as np
 import pytest
@@ -39,7 +44,9 @@ def shape(dk, swr=4):
 
 
 def range_bytes(n):
-    return min(n, INT32_MAX)
+    """The kernel's clamp to [0, INT32_MAX] (a negative range would be a huge
+    unsigned record count, which passes every offset)."""
+    return min(max(n, 0), INT32_MAX)
 
 
 def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows, swr=4):
@@ -73,9 +80,11 @@ def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows, swr=4):
                 assert (off >= 0).all() and (off + 4 <= rowb).all()
             for pw in range(NPROD):
                 t0 = pw * TPW
-                k = np.arange(nchunks)
+                k = np.arange(nchunks + 1)                               # one past the last chunk
                 rbase = k * CT + t0 - HR
-                xb = np.minimum(np.maximum(rbase, 0), L)
+                # issue(k): rows from min(rbase, L); issue_first's window
+                # path (rbase < 0): rows from 0
+                xb = np.where(rbase >= 0, np.minimum(rbase, L), 0)
                 base = (tb + xb) * rowb                                  # resource base (bytes of x)
                 rng = np.array([range_bytes((L - b) * rowb) for b in xb])
                 # the record count is an unsigned 32-bit field: a negative range
@@ -128,14 +137,18 @@ def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows, swr=4):
                         assert ((ow >= 0) & (ow + 4 <= HR * rowb))[inwin].all()
                         ox = np.where(r >= 0, r * rowb + cv, OUT_OF_RANGE)
                         n_checked += through(base[0], rng[0], ox, np.where(r >= 0, r, -1))
-                # gates: token k CT + lane % CT of head h
+                # gates: token k CT + lane % CT of head h, for wave 0 only
                 ht = Hv * 4
-                grec = np.array([range_bytes((L - kk * CT) * ht) for kk in k])
+                grec = np.array([range_bytes((L - kk * CT) * ht) if pw == 0 else 0 for kk in k])
+                grec = grec % 2**32
                 goff = (lane % CT) * ht
                 okg = goff[None, :] + 4 <= grec[:, None]
                 tok = k[:, None] * CT + (lane % CT)[None, :]
                 assert ((tok >= 0) & (tok < L))[okg].all()
-                assert (okg | (tok >= L)).all()
+                if pw == 0:
+                    assert (okg | (tok >= L)).all()
+                else:
+                    assert not okg.any()
     return n_checked
 
 

@@ -47,21 +47,28 @@
 //     the order in which a lane supplies them to a 16x16x32 MFMA (keys 32 c +
 //     4 (l / 16) + i and 32 c + 16 + 4 (l / 16) + i, i < 4, side by side), so
 //     a lane's operand is one 16-byte read and matches its state registers;
-//   - four conv waves prepare the chunks: raw inputs loaded into registers a
-//     chunk ahead, conv + SiLU, the L2-normalised q^ and k^ rows and v (per
-//     chunk c); one chunk later the chunk's Gram products k^ k^T and q^ k^T,
-//     L, its inverse T, the output mask M (as two key halves) and the decay
-//     products are formed: in a 64-column workgroup a fifth wave forms L and
-//     T (so that no wave carries both the conv and the inversion) and conv
-//     waves 1-3 the halves of M and the decay products; in a whole-head one
-//     conv waves 0-3 share all four parts.  Conv wave 0 also writes each
-//     chunk's gates and decay ratios.
+//   - eight conv waves prepare the chunks, two per 4 tokens: one takes the
+//     q channel pairs, the other the k pairs (one pair per lane, so that each
+//     norm is reduced within one wave), and each half of the slice's v.  Raw
+//     inputs are loaded into registers a chunk ahead, then conv + SiLU, the
+//     L2-normalised q^ and k^ rows and v (per chunk c); one chunk later the
+//     chunk's Gram products k^ k^T and q^ k^T, L, its inverse T, the output
+//     mask M (as two key halves) and the decay products are formed: in a
+//     64-column workgroup a wave of its own forms L and T (so that no wave
+//     carries both the conv and the inversion) and three q waves the halves
+//     of M and the decay products; in a whole-head one four conv waves share
+//     the four parts.  Conv wave 0 also writes each chunk's gates and decay
+//     ratios.  A wave issues its own instructions at a fraction of the SIMD's
+//     rate (two vector waves on one SIMD each keep their solo speed, and a
+//     bf16 MFMA on one wave barely slows the vector work of another), so the
+//     work of an interval is spread over many short waves.
 // A chunk is prepared in interval c (conv), finished in c + 1 (T, M, decays)
 // and consumed by the state waves in c + 2; one barrier ends each interval,
 // so q^/k^/v rows are triple-buffered and T, M and the coefficients double-
-// buffered (about 117 KB of LDS at head size 128: one workgroup per CU).  The state is plain at every chunk boundary (no running scale),
-// so a run split at a multiple of 16 tokens and resumed from the written-back
-// state gives the same bits as the straight run.
+// buffered (about 120 KB of LDS at head size 128: one workgroup per CU).
+// The state is plain at every chunk boundary (no running scale), so a run
+// split at a multiple of 16 tokens and resumed from the written-back state
+// gives the same bits as the straight run.
 //
 // The conv window is rewritten by a second small kernel after this one, so
 // that no workgroup of a sequence can overwrite the window another workgroup
@@ -87,9 +94,10 @@ struct PrefillShape {
     static constexpr int SW = NB < SWR ? NB : SWR; // state waves per workgroup, one block each
     static constexpr int NSL = NB / SW;        // workgroups per (sequence, v-head)
     static constexpr int ISZ = 16 * SW;        // value columns per workgroup
-    static constexpr int NPROD = 4;            // conv waves
-    // a wave of its own for the Gram products, T, M and the decay products
-    // when the workgroup is small enough (else the conv waves share them)
+    static constexpr int NPROD = 8;            // conv waves: q and k of 4 tokens each
+    // a wave of its own for L and T when the workgroup has room for it (the
+    // conv waves form the other finish parts, and all of them in a whole-head
+    // workgroup)
     static constexpr int NFIN = SW <= 4 ? 1 : 0;
     static constexpr int NT = 64 * (SW + NPROD + NFIN);
     static constexpr int WPE = (SW + NPROD + NFIN + 3) / 4; // waves per SIMD (one workgroup per CU)
@@ -100,12 +108,22 @@ struct PrefillShape {
     static constexpr int KTS = CT + 8;         // row stride of the bf16 transposed k^ rows
     static constexpr int TS = CT + 4;          // row stride of 16-wide fp32 rows (floats)
     static constexpr int QKP = DK / 2;         // q (and k) channel pairs
-    static constexpr int NVP = ISZ / 2;        // v channel pairs
-    static constexpr int TPW = CT / NPROD;     // tokens per producer wave
-    static constexpr int NVJ = (TPW * NVP + 63) / 64; // v conv jobs per producer lane
+    static constexpr int NVP = ISZ / 2;        // v channel pairs of the slice
+    static constexpr int TPW = 2 * CT / NPROD; // tokens per conv wave
+    static constexpr int NVW = NVP / 2;        // v pairs per conv wave (half the slice's)
+    static constexpr int NVJ = (TPW * NVW + 63) / 64; // v conv jobs per conv lane
+    // the finish part (see `finish`) conv wave pw forms, or -1: the lighter q
+    // waves take them, and wave 0 the gates and decay ratios
+    static constexpr int conv_part(int pw)
+    {
+        if (NFIN)
+            return pw == 2 ? 1 : pw == 4 ? 3 : pw == 6 ? 2 : -1;
+        return pw == 2 ? 0 : pw == 4 ? 1 : pw == 6 ? 3 : pw == 7 ? 2 : -1;
+    }
     static_assert(DK == DV, "square heads only");
     static_assert(DK % 16 == 0 && NB % SW == 0, "16-wide blocks");
-    static_assert(QKP <= 64, "one q/k channel pair per producer lane");
+    static_assert(QKP <= 64, "one q/k channel pair per conv lane");
+    static_assert(NVP % 2 == 0 && NPROD * TPW == 2 * CT, "two conv waves per token group");
 };
 
 // Per-chunk coefficients (rows of cf[2][CF_N][16]): for token t of the chunk
@@ -276,6 +294,7 @@ void prefill_kernel(PrefillParams p)
     using Sh = PrefillShape<DK, DV, SWR>;
     constexpr int CT = Sh::CT, NKB = Sh::NKB, SW = Sh::SW, ISZ = Sh::ISZ, KS = Sh::KS;
     constexpr int TS = Sh::TS, QKP = Sh::QKP, NVP = Sh::NVP, TPW = Sh::TPW, NVJ = Sh::NVJ;
+    constexpr int NVW = Sh::NVW;
     static_assert(KS % 8 == 0 && Sh::KTS % 4 == 0, "16- and 8-byte operand reads");
 
     // chunk c's rows are written in interval c, read by the Gram stage in
@@ -511,9 +530,11 @@ void prefill_kernel(PrefillParams p)
         float* tile = reinterpret_cast<float*>(page + p.ssm_off) + int64_t(h) * DK * DV;
         // s[kb][r] = S[key 16 kb + 4 q4 + r][column col0 + m16], at byte
         // eoff + (16 kb + r) DV 4 of the head's tile.  State I/O goes through
-        // buffer resources with the whole offset in the lane's VGPR, so that
-        // the (rare) checkpoint stores inside the chunk loop hold one resource
-        // and no addresses across it.
+        // buffer resources: the lane's offset eoff, the row r as the
+        // instruction's immediate offset and the block 16 kb in the scalar
+        // offset, so that the (rare) checkpoint stores inside the chunk loop
+        // hold one resource and one address register across it.  Every access
+        // lies inside the tile.
         const int eoff = ((4 * q4) * DV + col0 + m16) * 4;
         constexpr int kTileBytes = DK * DV * 4;
         v4f s[NKB];
@@ -528,7 +549,7 @@ void prefill_kernel(PrefillParams p)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     s[kb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                        rt_tile, eoff + (16 * kb + r) * DV * 4, 0, 0));
+                        rt_tile, eoff + r * DV * 4, 16 * kb * DV * 4, 0));
         }
         auto store_state = [&](__amdgpu_buffer_rsrc_t dst, const v4f (&x)[NKB]) {
 #pragma unroll
@@ -536,7 +557,7 @@ void prefill_kernel(PrefillParams p)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[kb][r]), dst,
-                                                          eoff + (16 * kb + r) * DV * 4, 0, 0);
+                                                          eoff + r * DV * 4, 16 * kb * DV * 4, 0);
         };
         const __amdgpu_buffer_rsrc_t rt_ck = __builtin_amdgcn_make_buffer_rsrc(
             ck_tile ? ck_tile : tile, short(0), ck_tile ? kTileBytes : 0, kBufferWord3);
@@ -658,8 +679,14 @@ void prefill_kernel(PrefillParams p)
         return;
     }
 
-    // ========================= producer waves ===============================
+    // ========================= conv waves ===================================
+    // Conv wave pw takes tokens [t0, t0 + TPW) of each chunk: the q channel
+    // pairs (pw even) or the k channel pairs (pw odd), one pair per lane, and
+    // half of the slice's v pairs, so that each of q^ and k^ is normalised
+    // within one wave.
     const int pw = wave - SW;
+    const int ty = pw & 1; // 0: q, 1: k
+    const int t0 = (pw >> 1) * TPW;
     const uint16_t* win = reinterpret_cast<const uint16_t*>(page + p.conv_off);
 
     // conv taps of the slice's channel pairs into LDS (read back per chunk, so
@@ -676,23 +703,25 @@ void prefill_kernel(PrefillParams p)
         return p.conv_b ? make_float2(bf16_to_f32(p.conv_b[c]), bf16_to_f32(p.conv_b[c + 1]))
                         : make_float2(0.f, 0.f);
     };
-    const int qkp = min(lane, QKP - 1); // q/k pair of the lane (clamped; idle lanes recompute)
-    const float2 bq = bias2(2 * qkp), bk = bias2(DK + 2 * qkp);
+    const int qkp = min(lane, QKP - 1);  // the lane's pair (clamped; idle lanes recompute)
+    const int xch = ty * DK + 2 * qkp;   // its first channel in the slice's channel order
+    const float2 bx = bias2(xch);
     // v job jj of the lane: token t0 + vi[jj] of the wave's TPW, pair vpj[jj]
+    // (of the wave's half of the slice's pairs)
     int vi[NVJ], vpj[NVJ];
     float2 bv[NVJ];
 #pragma unroll
     for (int jj = 0; jj < NVJ; ++jj) {
         const int j = lane + 64 * jj;
-        vi[jj] = j / NVP;
-        vpj[jj] = j % NVP;
+        vi[jj] = j / NVW;
+        vpj[jj] = ty * NVW + j % NVW;
         bv[jj] = bias2(2 * DK + 2 * vpj[jj]);
     }
 
     // Raw inputs of chunk k for this wave's TPW tokens, loaded into registers
-    // a chunk ahead: for q and k the lane's channel pair over the W-1 rows
-    // before the wave's first token and its TPW rows; for v the W rows of each
-    // job; the gates of token k CT + lane % CT.  All are buffer loads with the
+    // a chunk ahead: the lane's q or k channel pair over the W-1 rows before
+    // the wave's first token and its TPW rows; for v the W rows of each job;
+    // the gates of token k CT + lane % CT.  All are buffer loads with the
     // row in the lane's offset: the range check returns zero for rows past
     // the sequence's end and for the rows before its start when the sequence
     // is cold, whose window resource is empty, so no load waits on a branch
@@ -700,13 +729,12 @@ void prefill_kernel(PrefillParams p)
     // whose tokens the coefficients then leave out (b = 0, decay 1).
     constexpr int HR = W - 1, NR = HR + TPW;
     constexpr uint32_t kOutOfRange = 0xFFFFFFF0u; // past any num_records below
-    const int t0 = pw * TPW;
-    uint32_t xq[NR], xk[NR], xv[NVJ][W];
+    uint32_t xr[NR], xv[NVJ][W];
     float2 pg;
-    // byte offsets inside a row of x of the lane's q pair, k pair, and (from
-    // the wave's first row) of each v job's first row
+    // byte offsets inside a row of x of the lane's pair, and (from the wave's
+    // first row) of each v job's first row
     const int rowb = p.C * 2;
-    const int oq = chan(2 * qkp) * 2, ok = chan(DK + 2 * qkp) * 2;
+    const int ox = chan(xch) * 2;
     int ov[NVJ];
 #pragma unroll
     for (int jj = 0; jj < NVJ; ++jj)
@@ -725,10 +753,8 @@ void prefill_kernel(PrefillParams p)
     };
     auto load_rows = [&](__amdgpu_buffer_rsrc_t rs) {
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            xq[i] = ld(rs, oq + i * rowb);
-            xk[i] = ld(rs, ok + i * rowb);
-        }
+        for (int i = 0; i < NR; ++i)
+            xr[i] = ld(rs, ox + i * rowb);
 #pragma unroll
         for (int jj = 0; jj < NVJ; ++jj)
 #pragma unroll
@@ -738,7 +764,7 @@ void prefill_kernel(PrefillParams p)
     // chunk k >= 1: the wave's first row k CT + t0 - HR is not before the
     // sequence's start (L, an empty range, once past its end)
     auto issue = [&](int k) { load_rows(rows_resource(min(k * CT + t0 - HR, L))); };
-    // chunk 0: wave 0's first rows come from the window
+    // chunk 0: the first rows of the waves of tokens 0-3 come from the window
     auto issue_first = [&]() {
         const int rbase = t0 - HR;
         pg = load_gates(0, pw == 0);
@@ -746,14 +772,12 @@ void prefill_kernel(PrefillParams p)
             issue(0);
         } else {
             const __amdgpu_buffer_rsrc_t rs = rows_resource(0);
-            // the first chunk of wave 0: rows -HR .. -1 come from the window
             const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t*>(win), short(0), warm ? HR * rowb : 0, kBufferWord3);
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
                 const int r = i - HR; // rbase == -HR here
-                xq[i] = r < 0 ? ld(rw, (HR + r) * rowb + oq) : ld(rs, r * rowb + oq);
-                xk[i] = r < 0 ? ld(rw, (HR + r) * rowb + ok) : ld(rs, r * rowb + ok);
+                xr[i] = r < 0 ? ld(rw, (HR + r) * rowb + ox) : ld(rs, r * rowb + ox);
             }
 #pragma unroll
             for (int jj = 0; jj < NVJ; ++jj) {
@@ -768,12 +792,12 @@ void prefill_kernel(PrefillParams p)
         }
     };
 
-    // conv + SiLU of chunk k for the wave's tokens [t0, t0 + TPW): v into
-    // vt[k % 3] (transposed), the bf16 halves of q^ and k^ into qr / kr[k % 3]
-    // (and of k^ by key into kc[k % 3]) once the wave has reduced the 2 TPW
-    // sums |q|^2, |k|^2 of its tokens.  Every token is
-    // computed, also past the sequence's end.  Wave 0 also writes the gates
-    // and the decay ratios r(t, s) into gt / rt[k & 1].
+    // conv + SiLU of chunk k for the wave's tokens [t0, t0 + TPW): its v into
+    // vt[k % 3] (transposed), the bf16 halves of its q^ or k^ into qr / kr[k %
+    // 3] (and of k^ by key into kc[k % 3]) once the wave has reduced the TPW
+    // sums |q|^2 or |k|^2 of its tokens.  Every token is computed, also past
+    // the sequence's end.  Wave 0 also writes the gates and the decay ratios
+    // r(t, s) into gt / rt[k & 1].
     auto prepare = [&](int k) { // k < nchunks
         static_assert(TPW == 4, "the sums of 4 tokens are reduced together");
         const int b3 = k % 3;
@@ -792,27 +816,21 @@ void prefill_kernel(PrefillParams p)
             }
             va[jj] = make_float2(a0, a1);
         }
-        // q, k: the lane walks the wave's tokens over its register rows
-        float2 tq[W], tk[W];
+        // q or k: the lane walks the wave's tokens over its register rows
+        float2 tx[W];
 #pragma unroll
-        for (int w = 0; w < W; ++w) {
-            tq[w] = taps[w][qkp];
-            tk[w] = taps[w][QKP + qkp];
-        }
-        auto conv2 = [&](const float2 (&tw)[W], float2 b, const uint32_t (&xr)[NR], int i) {
-            float a0 = b.x, a1 = b.y;
-#pragma unroll
-            for (int w = 0; w < W; ++w) {
-                a0 = fmaf(tw[w].x, lo_bf16(xr[i + w]), a0);
-                a1 = fmaf(tw[w].y, hi_bf16(xr[i + w]), a1);
-            }
-            return make_float2(a0, a1);
-        };
-        float2 qv[TPW], kv[TPW];
+        for (int w = 0; w < W; ++w)
+            tx[w] = taps[w][ty * QKP + qkp];
+        float2 xs[TPW];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-            qv[i] = conv2(tq, bq, xq, i);
-            kv[i] = conv2(tk, bk, xk, i);
+            float a0 = bx.x, a1 = bx.y;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                a0 = fmaf(tx[w].x, lo_bf16(xr[i + w]), a0);
+                a1 = fmaf(tx[w].y, hi_bf16(xr[i + w]), a1);
+            }
+            xs[i] = make_float2(a0, a1);
         }
         // keep the loads below the sums: loads moved above them would need
         // registers of their own, and the copies into the loop's registers
@@ -827,14 +845,12 @@ void prefill_kernel(PrefillParams p)
                 vt[b3][2 * vpj[jj] + 1][tt] = silu(va[jj].y);
             }
         }
-        float sq[TPW], sk[TPW];
+        float ss[TPW];
         const bool own = lane < QKP;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-            qv[i] = make_float2(silu(qv[i].x), silu(qv[i].y));
-            kv[i] = make_float2(silu(kv[i].x), silu(kv[i].y));
-            sq[i] = own ? fmaf(qv[i].x, qv[i].x, qv[i].y * qv[i].y) : 0.f;
-            sk[i] = own ? fmaf(kv[i].x, kv[i].x, kv[i].y * kv[i].y) : 0.f;
+            xs[i] = make_float2(silu(xs[i].x), silu(xs[i].y));
+            ss[i] = own ? fmaf(xs[i].x, xs[i].x, xs[i].y * xs[i].y) : 0.f;
         }
         // wave sums: halves (tokens 0|1 and 2|3 share a register), then rows
         // (row j then holds token (0, 2, 1, 3)[j]), then within the rows
@@ -848,39 +864,32 @@ void prefill_kernel(PrefillParams p)
                                                            false, false);
             return __uint_as_float(r[0]) + __uint_as_float(r[1]);
         };
-        auto token_sums = [&](const float (&v)[TPW]) {
-            return group_sum<16>(fold_rows(fold_halves(v[0], v[1]), fold_halves(v[2], v[3])));
-        };
-        const float tsq = token_sums(sq), tsk = token_sums(sk);
+        const float tsum = group_sum<16>(fold_rows(fold_halves(ss[0], ss[1]), fold_halves(ss[2], ss[3])));
         // row j of the sums holds token (0, 2, 1, 3)[j]; lane i < 4 takes token i's
         const int src = 16 * (((lane & 1) << 1) | ((lane >> 1) & 1));
-        const float rq = p.scale * __builtin_amdgcn_rsqf(__shfl(tsq, src, 64) + p.eps);
-        const float rk = __builtin_amdgcn_rsqf(__shfl(tsk, src, 64) + p.eps);
+        const float rx = (ty == 0 ? p.scale : 1.f) * __builtin_amdgcn_rsqf(__shfl(tsum, src, 64) + p.eps);
         if (own) {
             // the lane's keys 2 lane and 2 lane + 1 sit side by side in a row
             const int kp = key_pos<Sh::X32>(2 * lane);
-            uint16_t kch[2][TPW], kcl[2][TPW];
+            uint16_t(*dst)[CT][KS] = ty == 0 ? qr[b3] : kr[b3];
+            uint16_t xh[2][TPW], xl[2][TPW];
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
-                const float fq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rq), i));
-                const float fk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rk), i));
-                uint16_t h0, l0, h1, l1;
-                split_bf16(qv[i].x * fq, h0, l0);
-                split_bf16(qv[i].y * fq, h1, l1);
-                *reinterpret_cast<uint32_t*>(&qr[b3][0][t0 + i][kp]) = h0 | (uint32_t(h1) << 16);
-                *reinterpret_cast<uint32_t*>(&qr[b3][1][t0 + i][kp]) = l0 | (uint32_t(l1) << 16);
-                split_bf16(kv[i].x * fk, kch[0][i], kcl[0][i]);
-                split_bf16(kv[i].y * fk, kch[1][i], kcl[1][i]);
-                *reinterpret_cast<uint32_t*>(&kr[b3][0][t0 + i][kp]) = kch[0][i] | (uint32_t(kch[1][i]) << 16);
-                *reinterpret_cast<uint32_t*>(&kr[b3][1][t0 + i][kp]) = kcl[0][i] | (uint32_t(kcl[1][i]) << 16);
+                const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rx), i));
+                split_bf16(xs[i].x * f, xh[0][i], xl[0][i]);
+                split_bf16(xs[i].y * f, xh[1][i], xl[1][i]);
+                *reinterpret_cast<uint32_t*>(&dst[0][t0 + i][kp]) = xh[0][i] | (uint32_t(xh[1][i]) << 16);
+                *reinterpret_cast<uint32_t*>(&dst[1][t0 + i][kp]) = xl[0][i] | (uint32_t(xl[1][i]) << 16);
             }
-            // k^ columns of the two keys over the wave's 4 tokens (one 8-byte store each)
+            if (ty == 1) {
+                // k^ columns of the two keys over the wave's 4 tokens (one 8-byte store each)
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                *reinterpret_cast<uint2*>(&kc[b3][0][2 * lane + e][t0]) =
-                    make_uint2(kch[e][0] | (uint32_t(kch[e][1]) << 16), kch[e][2] | (uint32_t(kch[e][3]) << 16));
-                *reinterpret_cast<uint2*>(&kc[b3][1][2 * lane + e][t0]) =
-                    make_uint2(kcl[e][0] | (uint32_t(kcl[e][1]) << 16), kcl[e][2] | (uint32_t(kcl[e][3]) << 16));
+                for (int e = 0; e < 2; ++e) {
+                    *reinterpret_cast<uint2*>(&kc[b3][0][2 * lane + e][t0]) =
+                        make_uint2(xh[e][0] | (uint32_t(xh[e][1]) << 16), xh[e][2] | (uint32_t(xh[e][3]) << 16));
+                    *reinterpret_cast<uint2*>(&kc[b3][1][2 * lane + e][t0]) =
+                        make_uint2(xl[e][0] | (uint32_t(xl[e][1]) << 16), xl[e][2] | (uint32_t(xl[e][3]) << 16));
+                }
             }
         }
         if (pw == 0)
@@ -890,17 +899,17 @@ void prefill_kernel(PrefillParams p)
 
     issue_first();
     __syncthreads(); // taps in LDS
-    const bool fin = !Sh::NFIN || pw >= 1; // a finish part of its own
+    const int fp = Sh::conv_part(pw); // the finish part this wave forms, or -1
     for (int c = 0; c < nchunks; ++c) {
         prepare(c); // also issues chunk c + 1's loads
-        if (c >= 1 && fin)
-            finish(c - 1, pw); // part pw of the previous chunk
+        if (c >= 1 && fp >= 0)
+            finish(c - 1, fp);
         __syncthreads(); // end of interval c
     }
     // intervals nchunks and nchunks + 1: the last chunk's finish parts, then
     // the state waves' last chunk
-    if (fin)
-        finish(nchunks - 1, pw);
+    if (fp >= 0)
+        finish(nchunks - 1, fp);
     __syncthreads();
     __syncthreads();
 }

@@ -26,21 +26,24 @@ kernel runs on a GPU.
 import numpy as np
 import pytest
 
-CT, NPROD = 16, 4
+CT, NPROD = 16, 8
 INT32_MAX = 2**31 - 1
 OUT_OF_RANGE = 0xFFFFFFF0
 
 
 def shape(dk, swr=4):
     """Column slice of a workgroup: up to `swr` 16-column blocks of the head
-    (4, or 8 for whole 128-column heads)."""
+    (4, or 8 for whole 128-column heads).  Eight conv waves: two per 4
+    tokens, one for the q pairs and one for the k pairs, each with half of
+    the slice's v pairs."""
     nb = dk // 16
     sw = min(nb, swr)
     isz = 16 * sw
-    tpw = CT // NPROD
+    tpw = 2 * CT // NPROD
     nvp = isz // 2
-    return dict(ISZ=isz, NSL=nb // sw, TPW=tpw, QKP=dk // 2, NVP=nvp,
-                NVJ=(tpw * nvp + 63) // 64)
+    nvw = nvp // 2
+    return dict(ISZ=isz, NSL=nb // sw, TPW=tpw, QKP=dk // 2, NVP=nvp, NVW=nvw,
+                NVJ=(tpw * nvw + 63) // 64)
 
 
 def range_bytes(n):
@@ -70,16 +73,17 @@ def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows, swr=4):
                                 np.where(ch < 2 * dk, Hk * dk + g * dk + (ch - dk),
                                          2 * Hk * dk + h * dk + sl * sh["ISZ"] + (ch - 2 * dk)))
             qkp = np.minimum(lane, sh["QKP"] - 1)
-            oq, ok = chan(2 * qkp) * 2, chan(dk + 2 * qkp) * 2
             jj = lane[None, :] + 64 * np.arange(sh["NVJ"])[:, None]     # [NVJ, 64]
-            vi, vpj = jj // sh["NVP"], jj % sh["NVP"]
-            cv = chan(2 * dk + 2 * vpj) * 2
-            ov = np.minimum(vi, TPW - 1) * rowb + cv
-            # every owned channel pair lies inside one row of x
-            for off in (oq, ok, cv):
-                assert (off >= 0).all() and (off + 4 <= rowb).all()
             for pw in range(NPROD):
-                t0 = pw * TPW
+                ty = pw & 1                                              # 0: q, 1: k
+                t0 = (pw >> 1) * TPW
+                ox = chan(ty * dk + 2 * qkp) * 2
+                vi, vpj = jj // sh["NVW"], ty * sh["NVW"] + jj % sh["NVW"]
+                cv = chan(2 * dk + 2 * vpj) * 2
+                ov = np.minimum(vi, TPW - 1) * rowb + cv
+                # every owned channel pair lies inside one row of x
+                for off in (ox, cv):
+                    assert (off >= 0).all() and (off + 4 <= rowb).all()
                 k = np.arange(nchunks + 1)                               # one past the last chunk
                 rbase = k * CT + t0 - HR
                 # issue(k): rows from min(rbase, L); issue_first's window
@@ -106,30 +110,29 @@ def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows, swr=4):
                 main = rbase >= 0
                 for i in range(NR):
                     row = rbase[:, None] + i                              # token row of load i
-                    for off in (oq, ok):
-                        n_checked += through(base[main, None], rng[main, None],
-                                             (off[None, :] + i * rowb)[np.zeros(main.sum(), int)],
-                                             row[main])
+                    n_checked += through(base[main, None], rng[main, None],
+                                         (ox[None, :] + i * rowb)[np.zeros(main.sum(), int)],
+                                         row[main])
                 for w in range(W):
                     row = rbase[:, None, None] + np.minimum(vi, TPW - 1)[None] + w
                     n_checked += through(base[main, None, None], rng[main, None, None],
                                          np.broadcast_to(ov + w * rowb, (main.sum(),) + ov.shape),
                                          row[main])
                 if (~main).any():
-                    # the first chunk of wave 0: rows before the start come from the window
-                    assert pw == 0 and rbase[0] == -HR and (~main).sum() == 1
+                    # the first chunk of the waves of tokens 0-3: rows before the
+                    # start come from the window
+                    assert pw < 2 and rbase[0] == -HR and (~main).sum() == 1
                     win_range = HR * rowb if warm else 0
                     for i in range(NR):
                         r = i - HR
-                        for off in (oq, ok):
-                            if r < 0:
-                                o = (HR + r) * rowb + off
-                                assert ((o >= 0) & (o + 4 <= HR * rowb)).all()
-                                if not warm:
-                                    assert win_range == 0
-                            else:
-                                n_checked += through(base[0], rng[0], r * rowb + off,
-                                                     np.full(64, r))
+                        if r < 0:
+                            o = (HR + r) * rowb + ox
+                            assert ((o >= 0) & (o + 4 <= HR * rowb)).all()
+                            if not warm:
+                                assert win_range == 0
+                        else:
+                            n_checked += through(base[0], rng[0], r * rowb + ox,
+                                                 np.full(64, r))
                     for w in range(W):
                         r = np.minimum(vi, TPW - 1) + w - HR
                         ow = np.where(r < 0, (HR + r) * rowb + cv, OUT_OF_RANGE)

@@ -57,8 +57,8 @@
 //     64-column workgroup a wave of its own forms L and T (so that no wave
 //     carries both the conv and the inversion) and three q waves the halves
 //     of M and the decay products; in a whole-head one four conv waves share
-//     the four parts.  Conv wave 0 also writes each chunk's gates and decay
-//     ratios.  A wave issues its own instructions at a fraction of the SIMD's
+//     the four parts.  One conv wave also writes each chunk's gates and
+//     decay ratios.  A wave issues its own instructions at a fraction of the SIMD's
 //     rate (two vector waves on one SIMD each keep their solo speed, and a
 //     bf16 MFMA on one wave barely slows the vector work of another), so the
 //     work of an interval is spread over many short waves.
@@ -112,14 +112,22 @@ struct PrefillShape {
     static constexpr int TPW = 2 * CT / NPROD; // tokens per conv wave
     static constexpr int NVW = NVP / 2;        // v pairs per conv wave (half the slice's)
     static constexpr int NVJ = (TPW * NVW + 63) / 64; // v conv jobs per conv lane
-    // the finish part (see `finish`) conv wave pw forms, or -1: the lighter q
-    // waves take them, and wave 0 the gates and decay ratios
+    // Roles of conv wave pw (wave SW + NFIN + pw of the workgroup, on SIMD
+    // (SW + NFIN + pw) % 4): its type (0: q, 1: k; the k waves also write
+    // the transposed rows, so they carry more), the finish part (see
+    // `finish`) it forms, or -1, and the one wave that writes the gates and
+    // decay ratios.  A SIMD issues one vector instruction per 4 cycles over
+    // all its waves, so the assignment evens out the SIMDs' instruction
+    // counts: with a finish wave, SIMD 0 also runs it and gets two q waves
+    // and no other part.
+    static constexpr int conv_type(int pw) { return NFIN ? (pw + 1) & 1 : pw & 1; }
     static constexpr int conv_part(int pw)
     {
         if (NFIN)
-            return pw == 2 ? 1 : pw == 4 ? 3 : pw == 6 ? 2 : -1;
-        return pw == 2 ? 0 : pw == 4 ? 1 : pw == 6 ? 3 : pw == 7 ? 2 : -1;
+            return pw == 1 ? 1 : pw == 0 ? 3 : pw == 2 ? 2 : -1;
+        return pw == 0 ? 0 : pw == 2 ? 1 : pw == 6 ? 3 : pw == 3 ? 2 : -1;
     }
+    static constexpr int RATIO_PW = NFIN ? 5 : 1;
     static_assert(DK == DV, "square heads only");
     static_assert(DK % 16 == 0 && NB % SW == 0, "16-wide blocks");
     static_assert(QKP <= 64, "one q/k channel pair per conv lane");
@@ -524,9 +532,13 @@ void prefill_kernel(PrefillParams p)
         }
     };
 
-    if (wave < SW) {
+    // roles by wave: the finish wave first (the oldest wave of a SIMD gets
+    // the first issue slot, and its substitution chain is the least able to
+    // wait), then the state waves, then the conv waves
+    const int sw = wave - Sh::NFIN; // state wave index, for sw in [0, SW)
+    if (sw >= 0 && sw < SW) {
         // ========================= state waves ==============================
-        const int col0 = sl * ISZ + 16 * wave; // first column of the block in the head
+        const int col0 = sl * ISZ + 16 * sw; // first column of the block in the head
         float* tile = reinterpret_cast<float*>(page + p.ssm_off) + int64_t(h) * DK * DV;
         // s[kb][r] = S[key 16 kb + 4 q4 + r][column col0 + m16], at byte
         // eoff + (16 kb + r) DV 4 of the head's tile.  State I/O goes through
@@ -607,7 +619,7 @@ void prefill_kernel(PrefillParams p)
                 // R[t] = b_t (v_t - A_t P_t), then D = T R
                 const float4 bb = *reinterpret_cast<const float4*>(&cf[b2][CF_B][4 * q4]);
                 const float4 aa = *reinterpret_cast<const float4*>(&cf[b2][CF_A][4 * q4]);
-                const float4 vv = *reinterpret_cast<const float4*>(&vt[b3][16 * wave + m16][4 * q4]);
+                const float4 vv = *reinterpret_cast<const float4*>(&vt[b3][16 * sw + m16][4 * q4]);
                 const float4 tt = *reinterpret_cast<const float4*>(&tm[b2][m16][4 * q4]);
                 const float R0 = bb.x * (vv.x - aa.x * P[0]);
                 const float R1 = bb.y * (vv.y - aa.y * P[1]);
@@ -629,7 +641,7 @@ void prefill_kernel(PrefillParams p)
                 O = mfma16(d[3], mv.w, O);
                 if (m16 < nt)
                     *reinterpret_cast<uint2*>(out_base + int64_t(k * CT + m16) * out_tok +
-                                              16 * wave + 4 * q4) = pack_bf16x4(O[0], O[1], O[2], O[3]);
+                                              16 * sw + 4 * q4) = pack_bf16x4(O[0], O[1], O[2], O[3]);
                 // S <- A_15 S_0 + sum_s r(15, s) k^_s d_s^T (and, for a checkpoint
                 // inside the chunk, the state after its first ck_m tokens): per
                 // 16-key block, K^T (16 keys x 16 tokens) times the decayed D
@@ -668,7 +680,7 @@ void prefill_kernel(PrefillParams p)
         return;
     }
 
-    if (Sh::NFIN && wave == SW + Sh::NPROD) {
+    if (Sh::NFIN && wave == 0) {
         // ========================= finish wave ==============================
         __syncthreads(); // the conv waves' taps are in LDS
         for (int c = 0; c < nchunks + 2; ++c) {
@@ -684,14 +696,15 @@ void prefill_kernel(PrefillParams p)
     // pairs (pw even) or the k channel pairs (pw odd), one pair per lane, and
     // half of the slice's v pairs, so that each of q^ and k^ is normalised
     // within one wave.
-    const int pw = wave - SW;
-    const int ty = pw & 1; // 0: q, 1: k
+    const int pw = wave - SW - Sh::NFIN;
+    const int ty = Sh::conv_type(pw); // 0: q, 1: k
+    const bool rw_ = pw == Sh::RATIO_PW; // writes the gates and decay ratios
     const int t0 = (pw >> 1) * TPW;
     const uint16_t* win = reinterpret_cast<const uint16_t*>(page + p.conv_off);
 
     // conv taps of the slice's channel pairs into LDS (read back per chunk, so
     // that they hold no registers across the loop); biases stay in registers
-    for (int e = tid - 64 * SW; e < W * (2 * QKP + NVP); e += 64 * Sh::NPROD) {
+    for (int e = tid - 64 * (SW + Sh::NFIN); e < W * (2 * QKP + NVP); e += 64 * Sh::NPROD) {
         const int w = e / (2 * QKP + NVP), pr = e - w * (2 * QKP + NVP);
         const int ch = pr < QKP ? 2 * pr : (pr < 2 * QKP ? DK + 2 * (pr - QKP) : 2 * DK + 2 * (pr - 2 * QKP));
         const int c = chan(ch);
@@ -767,7 +780,7 @@ void prefill_kernel(PrefillParams p)
     // chunk 0: the first rows of the waves of tokens 0-3 come from the window
     auto issue_first = [&]() {
         const int rbase = t0 - HR;
-        pg = load_gates(0, pw == 0);
+        pg = load_gates(0, rw_);
         if (rbase >= 0) {
             issue(0);
         } else {
@@ -796,7 +809,7 @@ void prefill_kernel(PrefillParams p)
     // vt[k % 3] (transposed), the bf16 halves of its q^ or k^ into qr / kr[k %
     // 3] (and of k^ by key into kc[k % 3]) once the wave has reduced the TPW
     // sums |q|^2 or |k|^2 of its tokens.  Every token is computed, also past
-    // the sequence's end.  Wave 0 also writes the gates and the decay ratios
+    // the sequence's end.  The ratio wave also writes the gates and the decay ratios
     // r(t, s) into gt / rt[k & 1].
     auto prepare = [&](int k) { // k < nchunks
         static_assert(TPW == 4, "the sums of 4 tokens are reduced together");
@@ -892,9 +905,9 @@ void prefill_kernel(PrefillParams p)
                 }
             }
         }
-        if (pw == 0)
+        if (rw_)
             write_ratios(k, pg);
-        pg = load_gates(k + 1, pw == 0); // after its last use, for the same reason
+        pg = load_gates(k + 1, rw_); // after its last use, for the same reason
     };
 
     issue_first();

@@ -42,8 +42,11 @@ def shape(dk, swr=4):
     tpw = 2 * CT // NPROD
     nvp = isz // 2
     nvw = nvp // 2
+    nfin = 1 if sw <= 4 else 0   # a finish wave of its own in the smaller workgroups
     return dict(ISZ=isz, NSL=nb // sw, TPW=tpw, QKP=dk // 2, NVP=nvp, NVW=nvw,
-                NVJ=(tpw * nvw + 63) // 64)
+                NVJ=(tpw * nvw + 63) // 64, NFIN=nfin,
+                TYPE=[((pw + 1) & 1) if nfin else (pw & 1) for pw in range(NPROD)],
+                RATIO_PW=5 if nfin else 1)
 
 
 def range_bytes(n):
@@ -75,7 +78,7 @@ def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows, swr=4):
             qkp = np.minimum(lane, sh["QKP"] - 1)
             jj = lane[None, :] + 64 * np.arange(sh["NVJ"])[:, None]     # [NVJ, 64]
             for pw in range(NPROD):
-                ty = pw & 1                                              # 0: q, 1: k
+                ty = sh["TYPE"][pw]                                      # 0: q, 1: k
                 t0 = (pw >> 1) * TPW
                 ox = chan(ty * dk + 2 * qkp) * 2
                 vi, vpj = jj // sh["NVW"], ty * sh["NVW"] + jj % sh["NVW"]
@@ -140,15 +143,16 @@ def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows, swr=4):
                         assert ((ow >= 0) & (ow + 4 <= HR * rowb))[inwin].all()
                         ox = np.where(r >= 0, r * rowb + cv, OUT_OF_RANGE)
                         n_checked += through(base[0], rng[0], ox, np.where(r >= 0, r, -1))
-                # gates: token k CT + lane % CT of head h, for wave 0 only
+                # gates: token k CT + lane % CT of head h, for the ratio wave only
                 ht = Hv * 4
-                grec = np.array([range_bytes((L - kk * CT) * ht) if pw == 0 else 0 for kk in k])
+                use = pw == sh["RATIO_PW"]
+                grec = np.array([range_bytes((L - kk * CT) * ht) if use else 0 for kk in k])
                 grec = grec % 2**32
                 goff = (lane % CT) * ht
                 okg = goff[None, :] + 4 <= grec[:, None]
                 tok = k[:, None] * CT + (lane % CT)[None, :]
                 assert ((tok >= 0) & (tok < L))[okg].all()
-                if pw == 0:
+                if use:
                     assert (okg | (tok >= L)).all()
                 else:
                     assert not okg.any()
@@ -200,3 +204,13 @@ def test_producer_loads_long_sequence():
     # one 65,536-token sequence after a 3-token one, at the end of x
     check_sequence(128, 4, 1, 2, 3, 0, warm=True, total_rows=65539)
     check_sequence(128, 4, 1, 2, 65536, 3, warm=False, total_rows=65539)
+
+
+@pytest.mark.parametrize("dk,swr", [(16, 4), (64, 4), (128, 4), (128, 8)])
+def test_every_token_group_has_a_q_and_a_k_wave(dk, swr):
+    # the two conv waves of 4 tokens (2 g, 2 g + 1) split q and k between them,
+    # and the ratio wave exists
+    sh = shape(dk, swr)
+    for g in range(NPROD // 2):
+        assert sorted(sh["TYPE"][2 * g: 2 * g + 2]) == [0, 1]
+    assert 0 <= sh["RATIO_PW"] < NPROD

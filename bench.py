@@ -533,7 +533,7 @@ def main():
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (3 times), the known-size "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters")
-    ap.add_argument("--only", choices=["prefill", "prefill32", "ceilings"],
+    ap.add_argument("--only", choices=["prefill", "prefill32", "ceilings", "restore"],
                     help="run one secondary leg alone and print its figures (for counter "
                          "passes under rocprofv3); no bench line")
     a = ap.parse_args()
@@ -561,6 +561,10 @@ def main():
             part = {"prefill_ms_p50": round(ppc["p50"], 4), "tokens": pinp.total_tokens}
         elif a.only == "prefill32":
             part = bench_prefill_32heads(a.steps, a.warmup)
+        elif a.only == "restore":
+            rms, rbytes, _, _, _, gs = bench_restore(a.steps, a.warmup)
+            part = {"restore_ms_p50": round(rms, 4), "restore_gb_per_s": round(rbytes / (rms * 1e-3) / 1e9, 2),
+                    "gather_gb_per_s": gs["gather"]["gb_per_s"], "scatter_gb_per_s": gs["scatter"]["gb_per_s"]}
         else:
             part = bench_ceilings()
         print(json.dumps({"only": a.only, **part}), flush=True)

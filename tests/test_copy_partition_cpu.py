@@ -35,8 +35,9 @@ def pieces(us, uw, n, G, w):
 
 
 def grid_for(us, uw, n, resident):
+    """Two resident rounds of workgroups, none with less than one block."""
     units = (us + uw) * n
-    return max(1, min(resident, -(-units // BLOCK_UNITS)))
+    return max(1, min(2 * resident, -(-units // BLOCK_UNITS)))
 
 
 @pytest.mark.parametrize("us,uw,n", [

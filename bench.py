@@ -155,7 +155,7 @@ def bench_decode(steps, warmup, extra_pad=0):
     return inp, ms, decode_bytes(inp), per_call(step, steps, stream)
 
 
-def bench_prefill(steps, warmup):
+def bench_prefill(steps, warmup, with_checkpoints=True):
     import torch
     import hybrid_linear_attention_slot_amd as gdn
     import workloads as wl
@@ -174,6 +174,8 @@ def bench_prefill(steps, warmup):
                                           inp.total_tokens, args, stream)
     timed(call, 1, max(1, warmup), stream)
     pc = per_call(call, max(2, steps), stream)
+    if not with_checkpoints:
+        return inp, pc, None
     # the same call emitting every sequence's state at its last 256-token block
     # boundary into a spare slot
     lens = np.diff(inp.cu_seqlens)
@@ -557,7 +559,7 @@ def main():
         torch.cuda.empty_cache()
     if a.only:
         if a.only == "prefill":
-            pinp, ppc, _ = bench_prefill(a.steps, a.warmup)
+            pinp, ppc, _ = bench_prefill(a.steps, a.warmup, with_checkpoints=False)
             part = {"prefill_ms_p50": round(ppc["p50"], 4), "tokens": pinp.total_tokens}
         elif a.only == "prefill32":
             part = bench_prefill_32heads(a.steps, a.warmup)
@@ -586,6 +588,10 @@ def main():
                "tflops": round(pflops, 2),
                "frac_of_fp32_vector_peak": round(pflops / FP32_VECTOR_PEAK_TFLOPS, 4),
                "frac_of_fp32_nonpacked_peak": round(pflops / FP32_NONPACKED_PEAK_TFLOPS, 4),
+               "arithmetic": "chunked delta rule (16-token chunks); products over the key "
+                             "dimension and the chunk's tokens as three bf16 MFMA products "
+                             "per fp32 product (hi*hi + hi*lo + lo*hi), fp32 accumulation; "
+                             "flops above are the recurrence's algorithmic fp32 flops",
                "workload": "8 seqs, lengths U{512..4096}, 16 v-heads/8 k-heads, 128x128 fp32, "
                            "4 warm + 4 cold",
                "ms_per_call_with_checkpoints": round(pms_ck, 4),

@@ -119,12 +119,12 @@ struct PrefillShape {
     // decay ratios.  A SIMD issues one vector instruction per 4 cycles over
     // all its waves, so the assignment evens out the SIMDs' instruction
     // counts: with a finish wave, SIMD 0 also runs it and gets two q waves
-    // and no other part.
+    // and one Gram half.
     static constexpr int conv_type(int pw) { return NFIN ? (pw + 1) & 1 : pw & 1; }
     static constexpr int conv_part(int pw)
     {
         if (NFIN)
-            return pw == 1 ? 1 : pw == 0 ? 3 : pw == 2 ? 2 : -1;
+            return pw == 3 ? 1 : pw == 0 ? 3 : pw == 2 ? 2 : -1;
         return pw == 0 ? 0 : pw == 2 ? 1 : pw == 6 ? 3 : pw == 3 ? 2 : -1;
     }
     static constexpr int RATIO_PW = NFIN ? 5 : 1;
@@ -322,6 +322,7 @@ void prefill_kernel(PrefillParams p)
     __shared__ __align__(16) float mm[2][2][CT][TS];
     __shared__ __align__(16) float cf[2][CF_N][CT]; // CF_* rows
     __shared__ __align__(16) float lw[CT][TS];      // L of the chunk being inverted
+    __shared__ __align__(16) float yw[8][12];       // C A^-1 of the chunk being inverted
     // conv taps of the slice's channel pairs, [tap][q pairs | k pairs | v pairs]
     __shared__ __align__(16) float2 taps[W][2 * QKP + NVP];
 
@@ -351,6 +352,10 @@ void prefill_kernel(PrefillParams p)
     const int tb = int(tb64);
     const int L = int(te64 - tb64);
     const int64_t out_tok = int64_t(p.Hv) * DV; // out elements per token
+    // T's upper-right 8 x 8 block is zero in every chunk: written once here,
+    // before the first barrier of every role
+    for (int e = tid; e < 2 * 8 * 8; e += Sh::NT)
+        tm[e >> 6][(e >> 3) & 7][8 + (e & 7)] = 0.f;
     uint16_t* out_base = p.out + int64_t(tb) * out_tok + int64_t(h) * DV + sl * ISZ;
     const int slot = p.state_indices[n];
     if (slot < 0 || slot >= p.num_slots) { // padding row: zero outputs, no state I/O
@@ -488,26 +493,51 @@ void prefill_kernel(PrefillParams p)
                 }
                 // the wave's own LDS writes above are read back by other lanes
                 lds_wave_sync();
-                // T = (I + L)^-1, column j = m16 in lane j (lanes 16-63 repeat it);
-                // the column index is opaque here so that the sixteen entries of
-                // the identity column are formed per chunk, not held across the
-                // chunk loop
-                int jc = m16;
-                asm volatile("" : "+v"(jc));
-                // T[t][j] = [t == j] - sum_{u<t} L[t][u] T[u][j]
-                float tc[CT];
+                // T = (I + L)^-1 in 8 x 8 blocks: with A and B the diagonal
+                // blocks of I + L and C its lower-left block,
+                //     T = [[A^-1, 0], [-B^-1 C A^-1, B^-1]]
+                // (T's upper-right block is zero from the kernel's start).
+                // (1) lane m16 (lanes 16-63 repeat it): column m16 % 8 of A^-1
+                // (m16 < 8) or B^-1 by forward substitution; the column index
+                // is opaque so that the identity entries are formed per chunk,
+                // not held across the chunk loop
+                {
+                    const int hb = 8 * (m16 >> 3);
+                    int jc = m16 & 7;
+                    asm volatile("" : "+v"(jc));
+                    float x[8];
 #pragma unroll
-                for (int t_ = 0; t_ < CT; ++t_) {
-                    float acc = t_ == jc ? 1.f : 0.f;
+                    for (int r = 0; r < 8; ++r) {
+                        float acc = r == jc ? 1.f : 0.f;
 #pragma unroll
-                    for (int u = 0; u < t_; ++u)
-                        acc = fmaf(-lw[t_][u], tc[u], acc);
-                    tc[t_] = acc;
+                        for (int c = 0; c < r; ++c)
+                            acc = fmaf(-lw[hb + r][hb + c], x[c], acc);
+                        x[r] = acc;
+                    }
+                    if (lane < CT) {
+#pragma unroll
+                        for (int r = 0; r < 8; ++r)
+                            tm[b2][hb + r][hb + (m16 & 7)] = x[r];
+                    }
                 }
-                if (lane < CT) {
+                lds_wave_sync();
+                // (2) Y = C A^-1 and (3) T's lower-left block -B^-1 Y, one
+                // entry (row lane / 8, column lane % 8) per lane
+                const int r8 = lane >> 3, c8 = lane & 7;
+                {
+                    float y = 0.f;
 #pragma unroll
-                    for (int t_ = 0; t_ < CT; ++t_)
-                        tm[b2][t_][lane] = tc[t_];
+                    for (int m = 0; m < 8; ++m)
+                        y = fmaf(lw[8 + r8][m], tm[b2][m][c8], y);
+                    yw[r8][c8] = y;
+                }
+                lds_wave_sync();
+                {
+                    float xv = 0.f;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m)
+                        xv = fmaf(tm[b2][8 + r8][8 + m], yw[m][c8], xv);
+                    tm[b2][8 + r8][c8] = -xv;
                 }
             } else {
 #pragma unroll

@@ -112,14 +112,15 @@ struct PrefillShape {
     static constexpr int TPW = 2 * CT / NPROD; // tokens per conv wave
     static constexpr int NVW = NVP / 2;        // v pairs per conv wave (half the slice's)
     static constexpr int NVJ = (TPW * NVW + 63) / 64; // v conv jobs per conv lane
-    // Roles of conv wave pw (wave SW + NFIN + pw of the workgroup, on SIMD
-    // (SW + NFIN + pw) % 4): its type (0: q, 1: k; the k waves also write
+    // Roles of conv wave pw (wave SW + 1 + pw of the workgroup with a finish
+    // wave; else wave 0 for pw = 0 and wave SW + pw; wave w runs on SIMD
+    // w % 4): its type (0: q, 1: k; the k waves also write
     // the transposed rows, so they carry more), the finish part (see
     // `finish`) it forms, or -1, and the one wave that writes the gates and
-    // decay ratios.  A SIMD issues one vector instruction per 4 cycles over
-    // all its waves, so the assignment evens out the SIMDs' instruction
-    // counts: with a finish wave, SIMD 0 also runs it and gets two q waves
-    // and one Gram half.
+    // decay ratios.  A SIMD shares its vector issue among its waves (older
+    // waves first; one wave alone reaches about half of it), so the
+    // assignment evens out the SIMDs' instruction counts: with a finish wave,
+    // SIMD 0 also runs it and gets two q waves and one Gram half.
     static constexpr int conv_type(int pw) { return NFIN ? (pw + 1) & 1 : pw & 1; }
     static constexpr int conv_part(int pw)
     {
@@ -562,10 +563,12 @@ void prefill_kernel(PrefillParams p)
         }
     };
 
-    // roles by wave: the finish wave first (the oldest wave of a SIMD gets
-    // the first issue slot, and its substitution chain is the least able to
-    // wait), then the state waves, then the conv waves
-    const int sw = wave - Sh::NFIN; // state wave index, for sw in [0, SW)
+    // roles by wave: the wave that inverts I + L first (the oldest wave of a
+    // SIMD gets the first issue slot, and its substitution chain is the least
+    // able to wait): the finish wave, or in a whole-head workgroup conv wave
+    // 0, which forms that part there; then the state waves (waves 1 .. SW),
+    // then the other conv waves
+    const int sw = wave - 1; // state wave index, for sw in [0, SW)
     if (sw >= 0 && sw < SW) {
         // ========================= state waves ==============================
         const int col0 = sl * ISZ + 16 * sw; // first column of the block in the head
@@ -726,7 +729,7 @@ void prefill_kernel(PrefillParams p)
     // pairs (pw even) or the k channel pairs (pw odd), one pair per lane, and
     // half of the slice's v pairs, so that each of q^ and k^ is normalised
     // within one wave.
-    const int pw = wave - SW - Sh::NFIN;
+    const int pw = Sh::NFIN ? wave - SW - 1 : (wave == 0 ? 0 : wave - SW);
     const int ty = Sh::conv_type(pw); // 0: q, 1: k
     const bool rw_ = pw == Sh::RATIO_PW; // writes the gates and decay ratios
     const int t0 = (pw >> 1) * TPW;
@@ -734,7 +737,7 @@ void prefill_kernel(PrefillParams p)
 
     // conv taps of the slice's channel pairs into LDS (read back per chunk, so
     // that they hold no registers across the loop); biases stay in registers
-    for (int e = tid - 64 * (SW + Sh::NFIN); e < W * (2 * QKP + NVP); e += 64 * Sh::NPROD) {
+    for (int e = 64 * pw + lane; e < W * (2 * QKP + NVP); e += 64 * Sh::NPROD) {
         const int w = e / (2 * QKP + NVP), pr = e - w * (2 * QKP + NVP);
         const int ch = pr < QKP ? 2 * pr : (pr < 2 * QKP ? DK + 2 * (pr - QKP) : 2 * DK + 2 * (pr - 2 * QKP));
         const int c = chan(ch);

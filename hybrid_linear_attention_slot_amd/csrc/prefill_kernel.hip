@@ -55,13 +55,15 @@
 //     chunk's Gram products k^ k^T and q^ k^T, L, its inverse T, the output
 //     mask M (as two key halves) and the decay products are formed: in a
 //     64-column workgroup a wave of its own forms L and T (so that no wave
-//     carries both the conv and the inversion) and three q waves the halves
-//     of M and the decay products; in a whole-head one four conv waves share
-//     the four parts.  One conv wave also writes each chunk's gates and
-//     decay ratios.  A wave issues its own instructions at a fraction of the SIMD's
-//     rate (two vector waves on one SIMD each keep their solo speed, and a
-//     bf16 MFMA on one wave barely slows the vector work of another), so the
-//     work of an interval is spread over many short waves.
+//     carries both the conv and the inversion) and three conv waves the
+//     halves of M and the decay products; in a whole-head one four conv
+//     waves share the four parts.  One conv wave also writes each chunk's
+//     gates and decay ratios.  A wave issues its own instructions at a
+//     fraction of the SIMD's rate (two vector waves on one SIMD each keep
+//     their solo speed, and a bf16 MFMA on one wave barely slows the vector
+//     work of another), so the work of an interval is spread over many short
+//     waves, and the wave that inverts I + L, whose chain waits on itself, is
+//     wave 0 (the oldest wave of a SIMD issues first).
 // A chunk is prepared in interval c (conv), finished in c + 1 (T, M, decays)
 // and consumed by the state waves in c + 2; one barrier ends each interval,
 // so q^/k^/v rows are triple-buffered and T, M and the coefficients double-
@@ -606,7 +608,7 @@ void prefill_kernel(PrefillParams p)
         };
         const __amdgpu_buffer_rsrc_t rt_ck = __builtin_amdgcn_make_buffer_rsrc(
             ck_tile ? ck_tile : tile, short(0), ck_tile ? kTileBytes : 0, kBufferWord3);
-        __syncthreads(); // the producers' taps are in LDS
+        __syncthreads(); // the conv waves' taps are in LDS
         for (int c = 0; c < nchunks + 2; ++c) {
             const int k = c - 2;
             if (k >= 0) {

@@ -129,3 +129,52 @@ def test_checkpoint_emission_full_size_equals_prefix_prefill():
     pay = g.conv_off + g.conv_region_bytes
     assert torch.equal(a.bufs[0][ck_t][:, :pay], c.bufs[0][idx_t][:, :pay])
     assert torch.equal(a.bufs[0][ck_t][:, pay:], b.bufs[0][ck_t][:, pay:])  # padding as it was
+
+
+def test_checkpoint_emission_in_whole_head_workgroups():
+    """Head size 128 in whole-head workgroups (the batch padded with empty
+    sequences past the GPU's compute units) emits the same checkpoint pages,
+    bit for bit, as in 64-column workgroups, and they match the oracle's
+    prefix runs."""
+    g = wl.make_geometry(96, Hk=4, Hv=8, dk=128, dv=128, W=4, page_align=128, extra_pad=128)
+    rng = wl.rng_for(777)
+    lens = [70, 33, 48, 17]
+    warm = np.array([1, 0, 1, 0], np.uint8)
+    perm = rng.permutation(g.num_slots - 8).astype(np.int32)
+    idx, spare = perm[:4], perm[4:8]
+    ck_len = np.array([23, 16, 48, 1], np.int32)  # mid-chunk, chunk edge, at the end, first token
+    img = wl.make_pool_image(g, rng, warm_slots=idx[warm == 1], nan_slots=idx[warm == 0], sigma_s=0.5)
+    inp = wl.step_inputs(g, rng, lens, idx, warm, bias=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_pad = cus // (2 * g.Hv) + 1 - len(lens)
+    assert len(lens) * g.Hv * 2 <= cus < (len(lens) + n_pad) * g.Hv * 2
+    padded = dataclasses.replace(
+        inp, cu_seqlens=np.concatenate([inp.cu_seqlens, np.full(n_pad, inp.cu_seqlens[-1], np.int32)]),
+        state_indices=np.concatenate([inp.state_indices,
+                                      np.arange(n_pad, dtype=np.int32) % 8 + g.num_slots - 8]),
+        has_initial_state=np.concatenate([inp.has_initial_state, np.zeros(n_pad, np.uint8)]))
+    pages = []
+    for what, run_inp, cks, ckl in (
+            ("64-column", inp, spare, ck_len),
+            ("whole-head", padded, np.concatenate([spare, np.full(n_pad, -1, np.int32)]),
+             np.concatenate([ck_len, np.zeros(n_pad, np.int32)]))):
+        dp = DevicePool(g, [img])
+        t = step_tensors(run_inp)
+        log(f"checkpoints in {what} workgroups ({run_inp.num_seqs} sequences)")
+        assert gdn.gdn_prefill_varlen_checkpoint(dp.pool, 0, run_inp.num_seqs, t["cu"],
+                                                 run_inp.max_seqlen, run_inp.total_tokens,
+                                                 args_of(t, run_inp), to_dev(cks.astype(np.int32)),
+                                                 to_dev(ckl.astype(np.int32))) == gdn.GDN_OK
+        torch.cuda.synchronize()
+        pages.append((dp.host(), u16(t["out"])))
+    (pa, oa), (pb, ob) = pages
+    assert np.array_equal(oa, ob), "outputs differ between shapes"
+    assert np.array_equal(pa, pb), "pages (sequences' and checkpoints') differ between shapes"
+    sub = dataclasses.replace(g, num_slots=1)
+    pad = slice(g.conv_off + g.conv_region_bytes, g.page_stride)
+    for n in range(len(lens)):
+        want = oracle_prefix_page(img, inp, n, int(ck_len[n]))
+        page = pb[spare[n]][None].copy()
+        assert np.array_equal(page[0, pad], img[spare[n], pad])
+        want[0, pad] = page[0, pad]
+        check_pages(sub, page, want, what=f"whole-head checkpoint of sequence {n}")

@@ -247,16 +247,22 @@ __device__ __forceinline__ v4f mfma_k16(bf16x4 a, bf16x4 b, v4f c)
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint16_t bf16_bits(float x)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// x = hi + lo to 16 significand bits for x0 and x1 at once: hi the bf16
+// rounding of x (nearest, ties to even), lo that of the exact remainder, as
+// packed pairs (x0's half in the low 16 bits), one pair conversion per half
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo)
 {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); // nearest, ties to even
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2v));
+    const f32x2 r = {x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u)};
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2v));
 }
-// x = hi + lo to 16 significand bits: hi the bf16 rounding of x, lo that of
-// the (exact) remainder
-__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo)
+// the low (kHi false) or high 16-bit halves of words w0 and w1 as one word (w0's first)
+template <bool kHi>
+__device__ __forceinline__ uint32_t halves(uint32_t w0, uint32_t w1)
 {
-    hi = bf16_bits(x);
-    lo = bf16_bits(x - __uint_as_float(uint32_t(hi) << 16));
+    return __builtin_amdgcn_perm(w1, w0, kHi ? 0x07060302u : 0x05040100u);
 }
 
 // The three products of a x b in bf16 halves (the lo x lo term, 2^-16 of it,
@@ -621,14 +627,14 @@ void prefill_kernel(PrefillParams p)
 #pragma unroll
                     for (int c2 = 0; c2 < Sh::NKC; ++c2) {
                         // the lane's 8 keys of the step: 32 c2 + 4 q4 + i, 32 c2 + 16 + 4 q4 + i
-                        bf16x8 sh, sl;
+                        // (element i = s[2 c2 + i / 4][i % 4], two per word)
+                        uint32_t h4[4], l4[4];
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            uint16_t hi, lo;
-                            split_bf16(s[2 * c2 + i / 4][i % 4], hi, lo);
-                            sh[i] = __builtin_bit_cast(__bf16, hi);
-                            sl[i] = __builtin_bit_cast(__bf16, lo);
-                        }
+                        for (int j = 0; j < 4; ++j)
+                            split_bf16x2(s[2 * c2 + j / 2][2 * (j % 2)], s[2 * c2 + j / 2][2 * (j % 2) + 1],
+                                         h4[j], l4[j]);
+                        const bf16x8 sh = __builtin_bit_cast(bf16x8, make_uint4(h4[0], h4[1], h4[2], h4[3]));
+                        const bf16x8 sl = __builtin_bit_cast(bf16x8, make_uint4(l4[0], l4[1], l4[2], l4[3]));
                         const int kp = 32 * c2 + 8 * q4;
                         auto ld8 = [&](const uint16_t* row) {
                             return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + kp));
@@ -637,14 +643,11 @@ void prefill_kernel(PrefillParams p)
                         O = mfma3_k32(sh, sl, ld8(qr[b3][0][m16]), ld8(qr[b3][1][m16]), O);
                     }
                 } else {
-                    bf16x4 sh, sl;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        uint16_t hi, lo;
-                        split_bf16(s[0][i], hi, lo);
-                        sh[i] = short(hi);
-                        sl[i] = short(lo);
-                    }
+                    uint32_t h2[2], l2[2];
+                    split_bf16x2(s[0][0], s[0][1], h2[0], l2[0]);
+                    split_bf16x2(s[0][2], s[0][3], h2[1], l2[1]);
+                    const bf16x4 sh = __builtin_bit_cast(bf16x4, make_uint2(h2[0], h2[1]));
+                    const bf16x4 sl = __builtin_bit_cast(bf16x4, make_uint2(l2[0], l2[1]));
                     auto ld4 = [&](const uint16_t* row) {
                         return __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(row + 4 * q4));
                     };
@@ -681,15 +684,11 @@ void prefill_kernel(PrefillParams p)
                 // inside the chunk, the state after its first ck_m tokens): per
                 // 16-key block, K^T (16 keys x 16 tokens) times the decayed D
                 auto advance = [&](v4f (&x)[NKB], float a0, const float4& e) {
-                    bf16x4 dh, dl;
-                    const float de[4] = {d[0] * e.x, d[1] * e.y, d[2] * e.z, d[3] * e.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        uint16_t hi, lo;
-                        split_bf16(de[i], hi, lo);
-                        dh[i] = short(hi);
-                        dl[i] = short(lo);
-                    }
+                    uint32_t h2[2], l2[2];
+                    split_bf16x2(d[0] * e.x, d[1] * e.y, h2[0], l2[0]);
+                    split_bf16x2(d[2] * e.z, d[3] * e.w, h2[1], l2[1]);
+                    const bf16x4 dh = __builtin_bit_cast(bf16x4, make_uint2(h2[0], h2[1]));
+                    const bf16x4 dl = __builtin_bit_cast(bf16x4, make_uint2(l2[0], l2[1]));
 #pragma unroll
                     for (int kb = 0; kb < NKB; ++kb) {
                         const bf16x4 kh4 = __builtin_bit_cast(
@@ -920,24 +919,26 @@ void prefill_kernel(PrefillParams p)
             // the lane's keys 2 lane and 2 lane + 1 sit side by side in a row
             const int kp = key_pos<Sh::X32>(2 * lane);
             uint16_t(*dst)[CT][KS] = ty == 0 ? qr[b3] : kr[b3];
-            uint16_t xh[2][TPW], xl[2][TPW];
+            // per token, the two keys' halves as one word each (key 2 lane in
+            // the low half)
+            uint32_t xh[TPW], xl[TPW];
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
                 const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rx), i));
-                split_bf16(xs[i].x * f, xh[0][i], xl[0][i]);
-                split_bf16(xs[i].y * f, xh[1][i], xl[1][i]);
-                *reinterpret_cast<uint32_t*>(&dst[0][t0 + i][kp]) = xh[0][i] | (uint32_t(xh[1][i]) << 16);
-                *reinterpret_cast<uint32_t*>(&dst[1][t0 + i][kp]) = xl[0][i] | (uint32_t(xl[1][i]) << 16);
+                split_bf16x2(xs[i].x * f, xs[i].y * f, xh[i], xl[i]);
+                *reinterpret_cast<uint32_t*>(&dst[0][t0 + i][kp]) = xh[i];
+                *reinterpret_cast<uint32_t*>(&dst[1][t0 + i][kp]) = xl[i];
             }
             if (ty == 1) {
                 // k^ columns of the two keys over the wave's 4 tokens (one 8-byte store each)
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    *reinterpret_cast<uint2*>(&kc[b3][0][2 * lane + e][t0]) =
-                        make_uint2(xh[e][0] | (uint32_t(xh[e][1]) << 16), xh[e][2] | (uint32_t(xh[e][3]) << 16));
-                    *reinterpret_cast<uint2*>(&kc[b3][1][2 * lane + e][t0]) =
-                        make_uint2(xl[e][0] | (uint32_t(xl[e][1]) << 16), xl[e][2] | (uint32_t(xl[e][3]) << 16));
-                }
+                *reinterpret_cast<uint2*>(&kc[b3][0][2 * lane][t0]) =
+                    make_uint2(halves<false>(xh[0], xh[1]), halves<false>(xh[2], xh[3]));
+                *reinterpret_cast<uint2*>(&kc[b3][0][2 * lane + 1][t0]) =
+                    make_uint2(halves<true>(xh[0], xh[1]), halves<true>(xh[2], xh[3]));
+                *reinterpret_cast<uint2*>(&kc[b3][1][2 * lane][t0]) =
+                    make_uint2(halves<false>(xl[0], xl[1]), halves<false>(xl[2], xl[3]));
+                *reinterpret_cast<uint2*>(&kc[b3][1][2 * lane + 1][t0]) =
+                    make_uint2(halves<true>(xl[0], xl[1]), halves<true>(xl[2], xl[3]));
             }
         }
         if (rw_)

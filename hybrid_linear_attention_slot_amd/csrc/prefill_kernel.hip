@@ -32,8 +32,9 @@
 // a_lo b_hi, exact bf16 x bf16 products accumulated in fp32 (operands carry
 // 16 of fp32's 24 significand bits; measured state error ~1e-5 of the
 // state's largest entry, against 1e-4 allowed).  A 16x16x32 bf16 MFMA costs
-// 16 cycles, a 16x16x4 fp32 MFMA (the same fp32 product over 4 keys) 32.
-// The two small 16x16 products of a chunk (T R and M D) stay in fp32.
+// 16 cycles, a 16x16x4 fp32 MFMA (the same fp32 product over 4 keys) 32, and
+// an fp32 MFMA stops the other waves' vector issue on its SIMD while it runs,
+// so the chunk's two 16x16 products (T R and D M^T) are split the same way.
 //
 // Parallel structure.  A workgroup takes one (sequence, v-head, slice of ISZ
 // value columns); its waves have two roles:
@@ -663,20 +664,29 @@ void prefill_kernel(PrefillParams p)
                 const float R1 = bb.y * (vv.y - aa.y * P[1]);
                 const float R2 = bb.z * (vv.z - aa.z * P[2]);
                 const float R3 = bb.w * (vv.w - aa.w * P[3]);
-                v4f d = {0.f, 0.f, 0.f, 0.f}; // d[r] = d_{4 q4 + r}[col0 + m16]
-                d = mfma16(tt.x, R0, d);
-                d = mfma16(tt.y, R1, d);
-                d = mfma16(tt.z, R2, d);
-                d = mfma16(tt.w, R3, d);
+                // d[r] = d_{4 q4 + r}[col0 + m16]: one 16x16x16 product, the lane
+                // holding T[m16][4 q4 + i] and R[4 q4 + i][m16] (bf16 splits: an
+                // fp32 MFMA would stop the other waves' vector issue on this SIMD)
+                auto split4 = [](float a, float b, float c, float e, bf16x4& h, bf16x4& l) {
+                    uint32_t h0, l0, h1, l1;
+                    split_bf16x2(a, b, h0, l0);
+                    split_bf16x2(c, e, h1, l1);
+                    h = __builtin_bit_cast(bf16x4, make_uint2(h0, h1));
+                    l = __builtin_bit_cast(bf16x4, make_uint2(l0, l1));
+                };
+                bf16x4 th, tl, rh, rl;
+                split4(tt.x, tt.y, tt.z, tt.w, th, tl);
+                split4(R0, R1, R2, R3, rh, rl);
+                const v4f d = mfma3_k16(th, tl, rh, rl, v4f{0.f, 0.f, 0.f, 0.f});
                 // outputs: O^T = A_t O^T + D^T M^T (lane: 4 columns of token m16)
                 const float4 m0 = *reinterpret_cast<const float4*>(&mm[b2][0][m16][4 * q4]);
                 const float4 m1 = *reinterpret_cast<const float4*>(&mm[b2][1][m16][4 * q4]);
                 const float4 mv = make_float4(m0.x + m1.x, m0.y + m1.y, m0.z + m1.z, m0.w + m1.w);
                 O *= cf[b2][CF_A][m16];
-                O = mfma16(d[0], mv.x, O);
-                O = mfma16(d[1], mv.y, O);
-                O = mfma16(d[2], mv.z, O);
-                O = mfma16(d[3], mv.w, O);
+                bf16x4 dh0, dl0, mh, ml;
+                split4(d[0], d[1], d[2], d[3], dh0, dl0);
+                split4(mv.x, mv.y, mv.z, mv.w, mh, ml);
+                O = mfma3_k16(dh0, dl0, mh, ml, O);
                 if (m16 < nt)
                     *reinterpret_cast<uint2*>(out_base + int64_t(k * CT + m16) * out_tok +
                                               16 * sw + 4 * q4) = pack_bf16x4(O[0], O[1], O[2], O[3]);

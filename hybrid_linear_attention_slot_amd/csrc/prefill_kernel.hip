@@ -44,15 +44,18 @@
 //     state into bf16 halves and forms P = K^ S_0 and S_0^T Q^^T (the state
 //     is the B operand of the first and the A operand of the second, so it
 //     never leaves the registers), R, D = T R with T = (I + L)^-1, the
-//     outputs, and the new state.  The q^ / k^ rows in LDS keep their keys in
+//     outputs, and the new state.  It also forms the v its R needs (lane l:
+//     column l % 16, tokens 4 (l / 16) + i) from its own loads of x, on the
+//     vector units beside the key products on the matrix cores.  The q^ / k^
+//     rows in LDS keep their keys in
 //     the order in which a lane supplies them to a 16x16x32 MFMA (keys 32 c +
 //     4 (l / 16) + i and 32 c + 16 + 4 (l / 16) + i, i < 4, side by side), so
 //     a lane's operand is one 16-byte read and matches its state registers;
 //   - eight conv waves prepare the chunks, two per 4 tokens: one takes the
 //     q channel pairs, the other the k pairs (one pair per lane, so that each
-//     norm is reduced within one wave), and each half of the slice's v.  Raw
-//     inputs are loaded into registers a chunk ahead, then conv + SiLU, the
-//     L2-normalised q^ and k^ rows and v (per chunk c); one chunk later the
+//     norm is reduced within one wave).  Raw inputs are loaded into registers
+//     a chunk ahead, then conv + SiLU and the L2-normalised q^ and k^ rows
+//     (per chunk c); one chunk later the
 //     chunk's Gram products k^ k^T and q^ k^T, L, its inverse T, the output
 //     mask M (as two key halves) and the decay products are formed: in a
 //     64-column workgroup a wave of its own forms L and T (so that no wave
@@ -67,8 +70,8 @@
 //     wave 0 (the oldest wave of a SIMD issues first).
 // A chunk is prepared in interval c (conv), finished in c + 1 (T, M, decays)
 // and consumed by the state waves in c + 2; one barrier ends each interval,
-// so q^/k^/v rows are triple-buffered and T, M and the coefficients double-
-// buffered (about 120 KB of LDS at head size 128: one workgroup per CU).
+// so q^/k^ rows are triple-buffered and T, M and the coefficients double-
+// buffered (about 104 KB of LDS at head size 128: one workgroup per CU).
 // The state is plain at every chunk boundary (no running scale), so a run
 // split at a multiple of 16 tokens and resumed from the written-back state
 // gives the same bits as the straight run.
@@ -111,10 +114,7 @@ struct PrefillShape {
     static constexpr int KTS = CT + 8;         // row stride of the bf16 transposed k^ rows
     static constexpr int TS = CT + 4;          // row stride of 16-wide fp32 rows (floats)
     static constexpr int QKP = DK / 2;         // q (and k) channel pairs
-    static constexpr int NVP = ISZ / 2;        // v channel pairs of the slice
     static constexpr int TPW = 2 * CT / NPROD; // tokens per conv wave
-    static constexpr int NVW = NVP / 2;        // v pairs per conv wave (half the slice's)
-    static constexpr int NVJ = (TPW * NVW + 63) / 64; // v conv jobs per conv lane
     // Roles of conv wave pw (wave SW + 1 + pw of the workgroup with a finish
     // wave; else wave 0 for pw = 0 and wave SW + pw; wave w runs on SIMD
     // w % 4): its type (0: q, 1: k; the k waves also write
@@ -135,7 +135,7 @@ struct PrefillShape {
     static_assert(DK == DV, "square heads only");
     static_assert(DK % 16 == 0 && NB % SW == 0, "16-wide blocks");
     static_assert(QKP <= 64, "one q/k channel pair per conv lane");
-    static_assert(NVP % 2 == 0 && NPROD * TPW == 2 * CT, "two conv waves per token group");
+    static_assert(NPROD * TPW == 2 * CT, "two conv waves per token group");
 };
 
 // Per-chunk coefficients (rows of cf[2][CF_N][16]): for token t of the chunk
@@ -311,8 +311,7 @@ void prefill_kernel(PrefillParams p)
 {
     using Sh = PrefillShape<DK, DV, SWR>;
     constexpr int CT = Sh::CT, NKB = Sh::NKB, SW = Sh::SW, ISZ = Sh::ISZ, KS = Sh::KS;
-    constexpr int TS = Sh::TS, QKP = Sh::QKP, NVP = Sh::NVP, TPW = Sh::TPW, NVJ = Sh::NVJ;
-    constexpr int NVW = Sh::NVW;
+    constexpr int TS = Sh::TS, QKP = Sh::QKP, TPW = Sh::TPW;
     static_assert(KS % 8 == 0 && Sh::KTS % 4 == 0, "16- and 8-byte operand reads");
 
     // chunk c's rows are written in interval c, read by the Gram stage in
@@ -323,7 +322,6 @@ void prefill_kernel(PrefillParams p)
     __shared__ __align__(16) uint16_t kr[3][2][CT][KS]; // k^ (L2-normalised)
     __shared__ __align__(16) uint16_t qr[3][2][CT][KS]; // q^ (normalised, times scale)
     __shared__ __align__(16) uint16_t kc[3][2][DK][Sh::KTS];
-    __shared__ __align__(16) float vt[3][ISZ][TS];  // v of the slice, [column][token]
     __shared__ __align__(16) float gt[2][2][CT];    // decay (1 past the end), beta (0 past it)
     __shared__ __align__(16) float rt[2][CT][TS];   // r(t, s) for s < t, 1 for s >= t
     __shared__ __align__(16) float tm[2][CT][TS];   // T = (I + L)^-1
@@ -333,8 +331,8 @@ void prefill_kernel(PrefillParams p)
     __shared__ __align__(16) float cf[2][CF_N][CT]; // CF_* rows
     __shared__ __align__(16) float lw[CT][TS];      // L of the chunk being inverted
     __shared__ __align__(16) float yw[8][12];       // C A^-1 of the chunk being inverted
-    // conv taps of the slice's channel pairs, [tap][q pairs | k pairs | v pairs]
-    __shared__ __align__(16) float2 taps[W][2 * QKP + NVP];
+    // conv taps of the q and k channel pairs, [tap][q pairs | k pairs]
+    __shared__ __align__(16) float2 taps[W][2 * QKP];
 
     // workgroup -> (k-head g, dispatch position of sequence n, v-head of the
     // group, slice): the workgroups of one (n, g) read the same q/k inputs and
@@ -377,6 +375,10 @@ void prefill_kernel(PrefillParams p)
     }
     const bool warm = p.hs[n] != 0;
     uint8_t* page = p.layer + int64_t(slot) * p.page_stride;
+    const uint16_t* win = reinterpret_cast<const uint16_t*>(page + p.conv_off);
+    const int rowb = p.C * 2;                     // bytes per row of x (and of the window)
+    constexpr uint32_t kOutOfRange = 0xFFFFFFF0u; // past any num_records below
+    constexpr int HR = W - 1;                     // window rows before a token
     const int nchunks = (L + CT - 1) / CT;
     auto chunk_len = [&](int k) { return min(CT, L - k * CT); };
 
@@ -615,12 +617,67 @@ void prefill_kernel(PrefillParams p)
         };
         const __amdgpu_buffer_rsrc_t rt_ck = __builtin_amdgcn_make_buffer_rsrc(
             ck_tile ? ck_tile : tile, short(0), ck_tile ? kTileBytes : 0, kBufferWord3);
+
+        // v of the block: lane l forms v[token 4 q4 + i][column col0 + m16],
+        // i < 4, itself (the values its R needs), from its channel's HR + 4
+        // rows, loaded one interval ahead with 16-bit buffer loads: the range
+        // check returns zero past the sequence's end, and the window rows of
+        // a cold sequence are an empty range.  The conv and SiLU run beside
+        // the key products on the matrix cores.
+        constexpr int NRV = HR + 4;
+        const int vch = chan(2 * DK + 16 * sw + m16); // the lane's v channel
+        const int vo = vch * 2;
+        float vtap[W];
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            vtap[w] = bf16_to_f32(p.conv_w[int64_t(vch) * W + w]);
+        const float vbias = p.conv_b ? bf16_to_f32(p.conv_b[vch]) : 0.f;
+        uint32_t vr[NRV]; // bf16 bits in the low half
+        auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
+            return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, int(off), 0, 0));
+        };
+        auto vrows = [&](int xb) { // rows of x from xb on (xb <= L)
+            return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x) + int64_t(tb + xb) * p.C,
+                                                     short(0), range_bytes(int64_t(L - xb) * rowb),
+                                                     kBufferWord3);
+        };
+        // chunk k >= 1: rows k CT - HR + 4 q4 + i, the first of them not before
+        // the sequence's start (L, an empty range, once past its end)
+        auto issue_v = [&](int k) {
+            const __amdgpu_buffer_rsrc_t rs = vrows(min(k * CT - HR, L));
+#pragma unroll
+            for (int i = 0; i < NRV; ++i)
+                vr[i] = ld16(rs, (4 * q4 + i) * rowb + vo);
+        };
+        { // chunk 0: the rows before the sequence's start come from the window
+            const __amdgpu_buffer_rsrc_t rs = vrows(0);
+            const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(win), short(0), warm ? HR * rowb : 0, kBufferWord3);
+#pragma unroll
+            for (int i = 0; i < NRV; ++i) {
+                const int r = 4 * q4 + i - HR;
+                vr[i] = ld16(rw, r < 0 ? uint32_t((HR + r) * rowb + vo) : kOutOfRange) |
+                        ld16(rs, r >= 0 ? uint32_t(r * rowb + vo) : kOutOfRange);
+            }
+        }
         __syncthreads(); // the conv waves' taps are in LDS
         for (int c = 0; c < nchunks + 2; ++c) {
             const int k = c - 2;
             if (k >= 0) {
                 const int b3 = k % 3, b2 = k & 1;
                 const int nt = chunk_len(k);
+                float vv[4]; // v[token 4 q4 + i][col0 + m16]
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float a = vbias;
+#pragma unroll
+                    for (int w = 0; w < W; ++w)
+                        a = fmaf(vtap[w], __uint_as_float(vr[i + w] << 16), a);
+                    vv[i] = silu(a);
+                }
+                // the next chunk's rows into the same registers, once read
+                __builtin_amdgcn_sched_barrier(0);
+                issue_v(k + 1);
                 // P[t][col] = k^_t . S_0[:, col]  (register r: token 4 q4 + r)
                 // O[col][t] = S_0[:, col] . q^_t  (register r: column 4 q4 + r, token m16)
                 v4f P = {0.f, 0.f, 0.f, 0.f}, O = {0.f, 0.f, 0.f, 0.f};
@@ -658,12 +715,11 @@ void prefill_kernel(PrefillParams p)
                 // R[t] = b_t (v_t - A_t P_t), then D = T R
                 const float4 bb = *reinterpret_cast<const float4*>(&cf[b2][CF_B][4 * q4]);
                 const float4 aa = *reinterpret_cast<const float4*>(&cf[b2][CF_A][4 * q4]);
-                const float4 vv = *reinterpret_cast<const float4*>(&vt[b3][16 * sw + m16][4 * q4]);
                 const float4 tt = *reinterpret_cast<const float4*>(&tm[b2][m16][4 * q4]);
-                const float R0 = bb.x * (vv.x - aa.x * P[0]);
-                const float R1 = bb.y * (vv.y - aa.y * P[1]);
-                const float R2 = bb.z * (vv.z - aa.z * P[2]);
-                const float R3 = bb.w * (vv.w - aa.w * P[3]);
+                const float R0 = bb.x * (vv[0] - aa.x * P[0]);
+                const float R1 = bb.y * (vv[1] - aa.y * P[1]);
+                const float R2 = bb.z * (vv[2] - aa.z * P[2]);
+                const float R3 = bb.w * (vv[3] - aa.w * P[3]);
                 // d[r] = d_{4 q4 + r}[col0 + m16]: one 16x16x16 product, the lane
                 // holding T[m16][4 q4 + i] and R[4 q4 + i][m16] (bf16 splits: an
                 // fp32 MFMA would stop the other waves' vector issue on this SIMD)
@@ -736,21 +792,19 @@ void prefill_kernel(PrefillParams p)
     }
 
     // ========================= conv waves ===================================
-    // Conv wave pw takes tokens [t0, t0 + TPW) of each chunk: the q channel
-    // pairs (pw even) or the k channel pairs (pw odd), one pair per lane, and
-    // half of the slice's v pairs, so that each of q^ and k^ is normalised
-    // within one wave.
+    // Conv wave pw takes tokens [t0, t0 + TPW) of each chunk: the q or the k
+    // channel pairs (conv_type), one pair per lane, so that each of q^ and
+    // k^ is normalised within one wave.
     const int pw = Sh::NFIN ? wave - SW - 1 : (wave == 0 ? 0 : wave - SW);
     const int ty = Sh::conv_type(pw); // 0: q, 1: k
     const bool rw_ = pw == Sh::RATIO_PW; // writes the gates and decay ratios
     const int t0 = (pw >> 1) * TPW;
-    const uint16_t* win = reinterpret_cast<const uint16_t*>(page + p.conv_off);
 
     // conv taps of the slice's channel pairs into LDS (read back per chunk, so
     // that they hold no registers across the loop); biases stay in registers
-    for (int e = 64 * pw + lane; e < W * (2 * QKP + NVP); e += 64 * Sh::NPROD) {
-        const int w = e / (2 * QKP + NVP), pr = e - w * (2 * QKP + NVP);
-        const int ch = pr < QKP ? 2 * pr : (pr < 2 * QKP ? DK + 2 * (pr - QKP) : 2 * DK + 2 * (pr - 2 * QKP));
+    for (int e = 64 * pw + lane; e < W * 2 * QKP; e += 64 * Sh::NPROD) {
+        const int w = e / (2 * QKP), pr = e - w * (2 * QKP);
+        const int ch = pr < QKP ? 2 * pr : DK + 2 * (pr - QKP);
         const int c = chan(ch);
         taps[w][pr] = make_float2(bf16_to_f32(p.conv_w[int64_t(c) * W + w]),
                                   bf16_to_f32(p.conv_w[int64_t(c + 1) * W + w]));
@@ -763,39 +817,20 @@ void prefill_kernel(PrefillParams p)
     const int qkp = min(lane, QKP - 1);  // the lane's pair (clamped; idle lanes recompute)
     const int xch = ty * DK + 2 * qkp;   // its first channel in the slice's channel order
     const float2 bx = bias2(xch);
-    // v job jj of the lane: token t0 + vi[jj] of the wave's TPW, pair vpj[jj]
-    // (of the wave's half of the slice's pairs)
-    int vi[NVJ], vpj[NVJ];
-    float2 bv[NVJ];
-#pragma unroll
-    for (int jj = 0; jj < NVJ; ++jj) {
-        const int j = lane + 64 * jj;
-        vi[jj] = j / NVW;
-        vpj[jj] = ty * NVW + j % NVW;
-        bv[jj] = bias2(2 * DK + 2 * vpj[jj]);
-    }
 
     // Raw inputs of chunk k for this wave's TPW tokens, loaded into registers
     // a chunk ahead: the lane's q or k channel pair over the W-1 rows before
-    // the wave's first token and its TPW rows; for v the W rows of each job;
-    // the gates of token k CT + lane % CT.  All are buffer loads with the
+    // the wave's first token and its TPW rows; the gates of token k CT + lane
+    // % CT.  All are buffer loads with the
     // row in the lane's offset: the range check returns zero for rows past
     // the sequence's end and for the rows before its start when the sequence
     // is cold, whose window resource is empty, so no load waits on a branch
     // and a cold page is never read.  Rows past the end give finite values
     // whose tokens the coefficients then leave out (b = 0, decay 1).
-    constexpr int HR = W - 1, NR = HR + TPW;
-    constexpr uint32_t kOutOfRange = 0xFFFFFFF0u; // past any num_records below
-    uint32_t xr[NR], xv[NVJ][W];
+    constexpr int NR = HR + TPW;
+    uint32_t xr[NR];
     float2 pg;
-    // byte offsets inside a row of x of the lane's pair, and (from the wave's
-    // first row) of each v job's first row
-    const int rowb = p.C * 2;
-    const int ox = chan(xch) * 2;
-    int ov[NVJ];
-#pragma unroll
-    for (int jj = 0; jj < NVJ; ++jj)
-        ov[jj] = min(vi[jj], TPW - 1) * rowb + chan(2 * DK + 2 * vpj[jj]) * 2;
+    const int ox = chan(xch) * 2; // byte offset of the lane's pair inside a row of x
     auto ld = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0);
     };
@@ -812,11 +847,6 @@ void prefill_kernel(PrefillParams p)
 #pragma unroll
         for (int i = 0; i < NR; ++i)
             xr[i] = ld(rs, ox + i * rowb);
-#pragma unroll
-        for (int jj = 0; jj < NVJ; ++jj)
-#pragma unroll
-            for (int w = 0; w < W; ++w)
-                xv[jj][w] = ld(rs, ov[jj] + w * rowb);
     };
     // chunk k >= 1: the wave's first row k CT + t0 - HR is not before the
     // sequence's start (L, an empty range, once past its end)
@@ -836,23 +866,13 @@ void prefill_kernel(PrefillParams p)
                 const int r = i - HR; // rbase == -HR here
                 xr[i] = r < 0 ? ld(rw, (HR + r) * rowb + ox) : ld(rs, r * rowb + ox);
             }
-#pragma unroll
-            for (int jj = 0; jj < NVJ; ++jj) {
-                const int cv = chan(2 * DK + 2 * vpj[jj]) * 2;
-#pragma unroll
-                for (int w = 0; w < W; ++w) {
-                    const int r = min(vi[jj], TPW - 1) + w - HR;
-                    xv[jj][w] = ld(rw, r < 0 ? uint32_t((HR + r) * rowb + cv) : kOutOfRange) |
-                                ld(rs, r >= 0 ? uint32_t(r * rowb + cv) : kOutOfRange);
-                }
-            }
         }
     };
 
-    // conv + SiLU of chunk k for the wave's tokens [t0, t0 + TPW): its v into
-    // vt[k % 3] (transposed), the bf16 halves of its q^ or k^ into qr / kr[k %
-    // 3] (and of k^ by key into kc[k % 3]) once the wave has reduced the TPW
-    // sums |q|^2 or |k|^2 of its tokens.  Every token is computed, also past
+    // conv + SiLU of chunk k for the wave's tokens [t0, t0 + TPW): the bf16
+    // halves of its q^ or k^ into qr / kr[k % 3] (and of k^ by key into
+    // kc[k % 3]) once the wave has reduced the TPW sums |q|^2 or |k|^2 of its
+    // tokens.  Every token is computed, also past
     // the sequence's end.  The ratio wave also writes the gates and the decay ratios
     // r(t, s) into gt / rt[k & 1].
     auto prepare = [&](int k) { // k < nchunks
@@ -861,18 +881,6 @@ void prefill_kernel(PrefillParams p)
         // the conv sums first: once they have read the raw rows, the next
         // chunk's loads go out (into the same registers) and have the rest of
         // the interval and the next one's start to arrive
-        float2 va[NVJ];
-#pragma unroll
-        for (int jj = 0; jj < NVJ; ++jj) {
-            float a0 = bv[jj].x, a1 = bv[jj].y;
-#pragma unroll
-            for (int w = 0; w < W; ++w) {
-                const float2 tw = taps[w][2 * QKP + vpj[jj]];
-                a0 = fmaf(tw.x, lo_bf16(xv[jj][w]), a0);
-                a1 = fmaf(tw.y, hi_bf16(xv[jj][w]), a1);
-            }
-            va[jj] = make_float2(a0, a1);
-        }
         // q or k: the lane walks the wave's tokens over its register rows
         float2 tx[W];
 #pragma unroll
@@ -894,14 +902,6 @@ void prefill_kernel(PrefillParams p)
         // would wait for the loads at the interval's end
         __builtin_amdgcn_sched_barrier(0);
         issue(k + 1);
-#pragma unroll
-        for (int jj = 0; jj < NVJ; ++jj) {
-            if (vi[jj] < TPW) {
-                const int tt = t0 + vi[jj];
-                vt[b3][2 * vpj[jj]][tt] = silu(va[jj].x);
-                vt[b3][2 * vpj[jj] + 1][tt] = silu(va[jj].y);
-            }
-        }
         float ss[TPW];
         const bool own = lane < QKP;
 #pragma unroll

@@ -1,9 +1,9 @@
 """CPU bounds model of the varlen prefill's producer loads (no GPU).
 
-The prefill kernel's producer waves read raw inputs with buffer loads whose
-range check returns zero past a resource's end, so every load either lies
-inside the rows of its own sequence (or its slot's window) or is refused by
-the range check.  A wrong row base or range here once let a wave read past
+The prefill kernel's conv waves (q and k rows) and state waves (each lane its
+own v channel) read raw inputs with buffer loads whose range check returns
+zero past a resource's end, so every load either lies inside the rows of its
+own sequence (or its slot's window) or is refused by the range check.  A wrong row base or range here once let a wave read past
 the end of x.  This test replays the producers' row / range / offset
 arithmetic for every head size and conv width the kernel is compiled for,
 over ragged lengths, and checks:
@@ -33,18 +33,15 @@ OUT_OF_RANGE = 0xFFFFFFF0
 
 def shape(dk, swr=4):
     """Column slice of a workgroup: up to `swr` 16-column blocks of the head
-    (4, or 8 for whole 128-column heads).  Eight conv waves: two per 4
-    tokens, one for the q pairs and one for the k pairs, each with half of
-    the slice's v pairs."""
+    (4, or 8 for whole 128-column heads), one state wave per block.  Eight
+    conv waves: two per 4 tokens, one for the q pairs and one for the k
+    pairs."""
     nb = dk // 16
     sw = min(nb, swr)
     isz = 16 * sw
     tpw = 2 * CT // NPROD
-    nvp = isz // 2
-    nvw = nvp // 2
     nfin = 1 if sw <= 4 else 0   # a finish wave of its own in the smaller workgroups
-    return dict(ISZ=isz, NSL=nb // sw, TPW=tpw, QKP=dk // 2, NVP=nvp, NVW=nvw,
-                NVJ=(tpw * nvw + 63) // 64, NFIN=nfin,
+    return dict(ISZ=isz, SW=sw, NSL=nb // sw, TPW=tpw, QKP=dk // 2, NFIN=nfin,
                 TYPE=[((pw + 1) & 1) if nfin else (pw & 1) for pw in range(NPROD)],
                 RATIO_PW=5 if nfin else 1)
 
@@ -56,17 +53,44 @@ def range_bytes(n):
 
 
 def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows, swr=4):
-    """All producer loads of all workgroups of one sequence."""
+    """All input loads (conv waves' q/k rows and gates, state waves' v rows)
+    of all workgroups of one sequence."""
     sh = shape(dk, swr)
     C = 2 * Hk * dk + Hv * dk
     rowb = 2 * C
     HR, TPW = W - 1, sh["TPW"]
-    NR = HR + TPW
+    NR = HR + TPW      # rows of a conv wave (4 tokens)
+    NRV = HR + 4       # rows of a state-wave lane (4 tokens)
     lane = np.arange(64)
+    q4, m16 = lane // 16, lane % 16
     nchunks = (L + CT - 1) // CT
     x_lo, x_hi = tb * rowb, (tb + L) * rowb          # the sequence's bytes of x
     assert x_hi <= total_rows * rowb
     n_checked = 0
+
+    def through(res_base, res_range, off, row_needed, size):
+        """Loads of `size` bytes at byte offsets `off` of the resource: the ones
+        the range check lets through must lie in the sequence's rows, and
+        every needed row must get through."""
+        off = np.asarray(off, np.int64) % 2**32                  # a VGPR offset is unsigned
+        ok_ = off + size <= res_range
+        addr = res_base + off
+        assert ((addr >= x_lo) & (addr + size <= x_hi))[ok_].all()
+        need = (row_needed >= 0) & (row_needed < L)
+        assert (ok_ | ~need).all(), "a row inside the sequence was refused"
+        return int(ok_.sum())
+
+    def window(r, off, size):
+        """Window loads at rows r < 0 (offsets off), else OUT_OF_RANGE."""
+        win_range = HR * rowb if warm else 0
+        ow = np.where(r < 0, (HR + r) * rowb + off, OUT_OF_RANGE)
+        inwin = ow + size <= win_range
+        assert ((ow >= 0) & (ow + size <= HR * rowb))[inwin].all()
+        if warm:
+            assert (inwin | (r >= 0)).all(), "a window row was refused"
+        else:
+            assert not inwin.any(), "a cold page was read"
+
     for h in range(Hv):
         g = h // (Hv // Hk)
         for sl in range(sh["NSL"]):
@@ -76,73 +100,37 @@ def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows, swr=4):
                                 np.where(ch < 2 * dk, Hk * dk + g * dk + (ch - dk),
                                          2 * Hk * dk + h * dk + sl * sh["ISZ"] + (ch - 2 * dk)))
             qkp = np.minimum(lane, sh["QKP"] - 1)
-            jj = lane[None, :] + 64 * np.arange(sh["NVJ"])[:, None]     # [NVJ, 64]
             for pw in range(NPROD):
                 ty = sh["TYPE"][pw]                                      # 0: q, 1: k
                 t0 = (pw >> 1) * TPW
                 ox = chan(ty * dk + 2 * qkp) * 2
-                vi, vpj = jj // sh["NVW"], ty * sh["NVW"] + jj % sh["NVW"]
-                cv = chan(2 * dk + 2 * vpj) * 2
-                ov = np.minimum(vi, TPW - 1) * rowb + cv
                 # every owned channel pair lies inside one row of x
-                for off in (ox, cv):
-                    assert (off >= 0).all() and (off + 4 <= rowb).all()
+                assert (ox >= 0).all() and (ox + 4 <= rowb).all()
                 k = np.arange(nchunks + 1)                               # one past the last chunk
                 rbase = k * CT + t0 - HR
                 # issue(k): rows from min(rbase, L); issue_first's window
                 # path (rbase < 0): rows from 0
                 xb = np.where(rbase >= 0, np.minimum(rbase, L), 0)
                 base = (tb + xb) * rowb                                  # resource base (bytes of x)
-                rng = np.array([range_bytes((L - b) * rowb) for b in xb])
                 # the record count is an unsigned 32-bit field: a negative range
                 # would pass every offset
-                rng = rng % 2**32
-
-                def through(res_base, res_range, off, row_needed):
-                    """Loads at byte offsets `off` of the resource: the ones the
-                    range check lets through must lie in the sequence's rows,
-                    and every needed row must get through."""
-                    off = np.asarray(off, np.int64) % 2**32              # a VGPR offset is unsigned
-                    ok_ = off + 4 <= res_range
-                    addr = res_base + off
-                    assert ((addr >= x_lo) & (addr + 4 <= x_hi))[ok_].all()
-                    need = (row_needed >= 0) & (row_needed < L)
-                    assert (ok_ | ~need).all(), "a row inside the sequence was refused"
-                    return int(ok_.sum())
-
+                rng = np.array([range_bytes((L - b) * rowb) for b in xb]) % 2**32
                 main = rbase >= 0
                 for i in range(NR):
                     row = rbase[:, None] + i                              # token row of load i
                     n_checked += through(base[main, None], rng[main, None],
                                          (ox[None, :] + i * rowb)[np.zeros(main.sum(), int)],
-                                         row[main])
-                for w in range(W):
-                    row = rbase[:, None, None] + np.minimum(vi, TPW - 1)[None] + w
-                    n_checked += through(base[main, None, None], rng[main, None, None],
-                                         np.broadcast_to(ov + w * rowb, (main.sum(),) + ov.shape),
-                                         row[main])
+                                         row[main], 4)
                 if (~main).any():
                     # the first chunk of the waves of tokens 0-3: rows before the
                     # start come from the window
                     assert pw < 2 and rbase[0] == -HR and (~main).sum() == 1
-                    win_range = HR * rowb if warm else 0
                     for i in range(NR):
-                        r = i - HR
-                        if r < 0:
-                            o = (HR + r) * rowb + ox
-                            assert ((o >= 0) & (o + 4 <= HR * rowb)).all()
-                            if not warm:
-                                assert win_range == 0
-                        else:
-                            n_checked += through(base[0], rng[0], r * rowb + ox,
-                                                 np.full(64, r))
-                    for w in range(W):
-                        r = np.minimum(vi, TPW - 1) + w - HR
-                        ow = np.where(r < 0, (HR + r) * rowb + cv, OUT_OF_RANGE)
-                        inwin = ow + 4 <= win_range
-                        assert ((ow >= 0) & (ow + 4 <= HR * rowb))[inwin].all()
-                        ox = np.where(r >= 0, r * rowb + cv, OUT_OF_RANGE)
-                        n_checked += through(base[0], rng[0], ox, np.where(r >= 0, r, -1))
+                        r = np.full(64, i - HR)
+                        window(r, ox, 4)
+                        n_checked += through(base[0], rng[0],
+                                             np.where(r >= 0, r * rowb + ox, OUT_OF_RANGE),
+                                             np.where(r >= 0, r, -1), 4)
                 # gates: token k CT + lane % CT of head h, for the ratio wave only
                 ht = Hv * 4
                 use = pw == sh["RATIO_PW"]
@@ -156,6 +144,28 @@ def check_sequence(dk, W, Hk, Hv, L, tb, warm, total_rows, swr=4):
                     assert (okg | (tok >= L)).all()
                 else:
                     assert not okg.any()
+            # state waves: lane (q4, m16) of state wave sw loads the rows of its
+            # v channel (16-bit loads) that tokens 4 q4 .. 4 q4 + 3 need
+            for sw in range(sh["SW"]):
+                vo = chan(2 * dk + 16 * sw + m16) * 2
+                assert (vo >= 0).all() and (vo + 2 <= rowb).all()
+                assert len(set(vo.tolist())) == 16                       # one column per m16
+                k = np.arange(1, nchunks + 1)                            # issue_v(k + 1) after chunk k
+                xb = np.minimum(k * CT - HR, L)
+                assert (xb >= 0).all()
+                base = (tb + xb) * rowb
+                rng = np.array([range_bytes((L - b) * rowb) for b in xb]) % 2**32
+                for i in range(NRV):
+                    off = (4 * q4 + i) * rowb + vo
+                    row = xb[:, None] + (4 * q4 + i)[None, :]
+                    n_checked += through(base[:, None], rng[:, None], off[None, :], row, 2)
+                # chunk 0: rows before the start from the window
+                rng0 = range_bytes(L * rowb) % 2**32
+                for i in range(NRV):
+                    r = 4 * q4 + i - HR
+                    window(r, vo, 2)
+                    n_checked += through(tb * rowb, rng0, np.where(r >= 0, r * rowb + vo, OUT_OF_RANGE),
+                                         np.where(r >= 0, r, -1), 2)
     return n_checked
 
 

@@ -123,12 +123,12 @@ struct PrefillShape {
     // decay ratios.  A SIMD shares its vector issue among its waves (older
     // waves first; one wave alone reaches about half of it), so the
     // assignment evens out the SIMDs' instruction counts: with a finish wave,
-    // SIMD 0 also runs it and gets two q waves and one Gram half.
+    // SIMD 0 also runs it and gets two q waves and no other part.
     static constexpr int conv_type(int pw) { return NFIN ? (pw + 1) & 1 : pw & 1; }
     static constexpr int conv_part(int pw)
     {
         if (NFIN)
-            return pw == 3 ? 1 : pw == 0 ? 3 : pw == 2 ? 2 : -1;
+            return pw == 1 ? 1 : pw == 0 ? 3 : pw == 2 ? 2 : -1;
         return pw == 0 ? 0 : pw == 2 ? 1 : pw == 6 ? 3 : pw == 3 ? 2 : -1;
     }
     static constexpr int RATIO_PW = NFIN ? 5 : 1;

@@ -107,11 +107,14 @@ struct PrefillShape {
     static constexpr int NFIN = SW <= 4 ? 1 : 0;
     static constexpr int NT = 64 * (SW + NPROD + NFIN);
     static constexpr int WPE = (SW + NPROD + NFIN + 3) / 4; // waves per SIMD (one workgroup per CU)
-    static constexpr bool X32 = DK >= 32;      // key products on 16x16x32 (else 16x16x16) MFMAs
+    static constexpr bool X32 = DK >= 32;      // key products in 32-key MFMA steps (else one 16-key step)
     static constexpr int KG = X32 ? 32 : 16;   // keys per MFMA step
     static constexpr int NKC = DK / KG;        // MFMA steps over the keys
     static constexpr int KS = DK + 8;          // row stride of the bf16 q^ / k^ rows (elements)
-    static constexpr int KTS = CT + 8;         // row stride of the bf16 transposed k^ rows
+    // row stride of the transposed k^ rows (elements): per token group of 4,
+    // the 4 hi and then the 4 lo halves (16 bytes); 80 bytes, so that the
+    // 16-byte reads of 8 consecutive rows hit distinct banks
+    static constexpr int KTS = 5 * 8;
     static constexpr int TS = CT + 4;          // row stride of 16-wide fp32 rows (floats)
     static constexpr int QKP = DK / 2;         // q (and k) channel pairs
     static constexpr int TPW = 2 * CT / NPROD; // tokens per conv wave
@@ -225,27 +228,16 @@ __device__ __forceinline__ float row_shr_or_one(float v)
                                                       0x110 + N, 0xF, 0xF, false));
 }
 
-// D = A B + C on a 16x16x4 fp32 tile: lane l supplies A[l % 16][l / 16] and
-// B[l / 16][l % 16] and holds D[4 (l / 16) + r][l % 16] in register r.
-__device__ __forceinline__ v4f mfma16(float a, float b, v4f c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short bf16x4 __attribute__((ext_vector_type(4))); // bit patterns
 
 // 16x16x32 bf16: lane l supplies A[l % 16][8 (l / 16) + i] and
-// B[8 (l / 16) + i][l % 16], i < 8; 16x16x16 bf16: A[l % 16][4 (l / 16) + i]
-// and B[4 (l / 16) + i][l % 16], i < 4; both hold D as mfma16 does.  (Lane
-// layouts and costs measured on gfx950: 16 cycles each, 32 for mfma16.)
+// B[8 (l / 16) + i][l % 16], i < 8, and holds D[4 (l / 16) + r][l % 16] in
+// register r.  (Lane layout and cost measured on gfx950: 16 cycles, as for
+// a 16x16x16 bf16 product; 32 for a 16x16x4 fp32 one.)
 __device__ __forceinline__ v4f mfma_k32(bf16x8 a, bf16x8 b, v4f c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ v4f mfma_k16(bf16x4 a, bf16x4 b, v4f c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -274,11 +266,29 @@ __device__ __forceinline__ v4f mfma3_k32(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8
     c = mfma_k32(ah, bl, c);
     return mfma_k32(al, bh, c);
 }
+// [x | y] as a lane's 8 slots of a 16x16x32 operand
+__device__ __forceinline__ bf16x8 pair(bf16x4 x, bf16x4 y)
+{
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// The same three products of 16x16x16 operands in two 16x16x32 products:
+// their summation slots are a dummy index, so lane l's eight slots can carry
+// its four a_hi and then its four a_lo entries (a = [a_hi | a_lo]) against
+// its four b_hi entries twice (bb = [b_hi | b_hi]): a_hi b_hi + a_lo b_hi;
+// and against [b_lo | 0] (blz): a_hi b_lo.  One 16x16x32 product costs what
+// a 16x16x16 one does.  Both are the same instruction on purpose: a
+// 16x16x16 product accumulating onto a 16x16x32 one's result (or the
+// reverse) with the compiler's wait states between them gave wrong sums on
+// gfx950 (measured), while chains of one instruction are exact.
+__device__ __forceinline__ v4f mfma3_k16(bf16x8 a, bf16x8 bb, bf16x8 blz, v4f c)
+{
+    c = mfma_k32(a, blz, c);
+    return mfma_k32(a, bb, c);
+}
+__device__ __forceinline__ bf16x8 lo_zero(bf16x4 x) { return pair(x, bf16x4{0, 0, 0, 0}); }
 __device__ __forceinline__ v4f mfma3_k16(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl, v4f c)
 {
-    c = mfma_k16(ah, bh, c);
-    c = mfma_k16(ah, bl, c);
-    return mfma_k16(al, bh, c);
+    return mfma3_k16(pair(ah, al), pair(bh, bh), lo_zero(bl), c);
 }
 
 // LDS values one lane of a wave wrote, read by other lanes of the same wave:
@@ -312,16 +322,17 @@ void prefill_kernel(PrefillParams p)
     using Sh = PrefillShape<DK, DV, SWR>;
     constexpr int CT = Sh::CT, NKB = Sh::NKB, SW = Sh::SW, ISZ = Sh::ISZ, KS = Sh::KS;
     constexpr int TS = Sh::TS, QKP = Sh::QKP, TPW = Sh::TPW;
-    static_assert(KS % 8 == 0 && Sh::KTS % 4 == 0, "16- and 8-byte operand reads");
+    static_assert(KS % 8 == 0 && Sh::KTS % 8 == 0, "16-byte operand reads");
 
     // chunk c's rows are written in interval c, read by the Gram stage in
     // c + 1 and by the state waves in c + 2: three buffers; T, M and the
     // coefficients are written in c + 1 and read in c + 2: two buffers
     // bf16 halves of the q^ / k^ rows ([hi, lo][token][key position]) and of
-    // the k^ columns ([hi, lo][key][token]) for the state update
+    // the k^ columns for the state update ([key][8 (t / 4) + i]: the hi
+    // halves of tokens 4 (t / 4) .. + 3 for i < 4, then their lo halves)
     __shared__ __align__(16) uint16_t kr[3][2][CT][KS]; // k^ (L2-normalised)
     __shared__ __align__(16) uint16_t qr[3][2][CT][KS]; // q^ (normalised, times scale)
-    __shared__ __align__(16) uint16_t kc[3][2][DK][Sh::KTS];
+    __shared__ __align__(16) uint16_t kc[3][DK][Sh::KTS];
     __shared__ __align__(16) float gt[2][2][CT];    // decay (1 past the end), beta (0 past it)
     __shared__ __align__(16) float rt[2][CT][TS];   // r(t, s) for s < t, 1 for s >= t
     __shared__ __align__(16) float tm[2][CT][TS];   // T = (I + L)^-1
@@ -755,13 +766,13 @@ void prefill_kernel(PrefillParams p)
                     split_bf16x2(d[2] * e.z, d[3] * e.w, h2[1], l2[1]);
                     const bf16x4 dh = __builtin_bit_cast(bf16x4, make_uint2(h2[0], h2[1]));
                     const bf16x4 dl = __builtin_bit_cast(bf16x4, make_uint2(l2[0], l2[1]));
+                    const bf16x8 dd = pair(dh, dh), dlz = lo_zero(dl);
 #pragma unroll
                     for (int kb = 0; kb < NKB; ++kb) {
-                        const bf16x4 kh4 = __builtin_bit_cast(
-                            bf16x4, *reinterpret_cast<const uint2*>(&kc[b3][0][16 * kb + m16][4 * q4]));
-                        const bf16x4 kl4 = __builtin_bit_cast(
-                            bf16x4, *reinterpret_cast<const uint2*>(&kc[b3][1][16 * kb + m16][4 * q4]));
-                        x[kb] = mfma3_k16(kh4, kl4, dh, dl, s[kb] * a0);
+                        // k^_hi and k^_lo of key 16 kb + m16, tokens 4 q4 .. + 3
+                        const bf16x8 k8 = __builtin_bit_cast(
+                            bf16x8, *reinterpret_cast<const uint4*>(&kc[b3][16 * kb + m16][8 * q4]));
+                        x[kb] = mfma3_k16(k8, dd, dlz, s[kb] * a0);
                     }
                 };
                 if (k == ck_c && ck_mid) {
@@ -941,14 +952,12 @@ void prefill_kernel(PrefillParams p)
             }
             if (ty == 1) {
                 // k^ columns of the two keys over the wave's 4 tokens (one 8-byte store each)
-                *reinterpret_cast<uint2*>(&kc[b3][0][2 * lane][t0]) =
-                    make_uint2(halves<false>(xh[0], xh[1]), halves<false>(xh[2], xh[3]));
-                *reinterpret_cast<uint2*>(&kc[b3][0][2 * lane + 1][t0]) =
-                    make_uint2(halves<true>(xh[0], xh[1]), halves<true>(xh[2], xh[3]));
-                *reinterpret_cast<uint2*>(&kc[b3][1][2 * lane][t0]) =
-                    make_uint2(halves<false>(xl[0], xl[1]), halves<false>(xl[2], xl[3]));
-                *reinterpret_cast<uint2*>(&kc[b3][1][2 * lane + 1][t0]) =
-                    make_uint2(halves<true>(xl[0], xl[1]), halves<true>(xl[2], xl[3]));
+                *reinterpret_cast<uint4*>(&kc[b3][2 * lane][2 * t0]) =
+                    make_uint4(halves<false>(xh[0], xh[1]), halves<false>(xh[2], xh[3]),
+                               halves<false>(xl[0], xl[1]), halves<false>(xl[2], xl[3]));
+                *reinterpret_cast<uint4*>(&kc[b3][2 * lane + 1][2 * t0]) =
+                    make_uint4(halves<true>(xh[0], xh[1]), halves<true>(xh[2], xh[3]),
+                               halves<true>(xl[0], xl[1]), halves<true>(xl[2], xl[3]));
             }
         }
         if (rw_)

@@ -812,17 +812,22 @@ void prefill_kernel(PrefillParams p)
     const int t0 = (pw >> 1) * TPW;
 
     // conv taps of the slice's channel pairs into LDS (read back per chunk, so
-    // that they hold no registers across the loop); biases stay in registers
+    // that they hold no registers across the loop); biases stay in registers.
+    // Both are scaled by -log2(e), so that a conv sum is y = -log2(e) x and
+    // the SiLU's exponential is exp2(y) with no multiply; the factor cancels
+    // in the L2 norm (see `prepare`).
+    constexpr float kNegLog2e = -1.4426950408889634f;
     for (int e = 64 * pw + lane; e < W * 2 * QKP; e += 64 * Sh::NPROD) {
         const int w = e / (2 * QKP), pr = e - w * (2 * QKP);
         const int ch = pr < QKP ? 2 * pr : DK + 2 * (pr - QKP);
         const int c = chan(ch);
-        taps[w][pr] = make_float2(bf16_to_f32(p.conv_w[int64_t(c) * W + w]),
-                                  bf16_to_f32(p.conv_w[int64_t(c + 1) * W + w]));
+        taps[w][pr] = make_float2(kNegLog2e * bf16_to_f32(p.conv_w[int64_t(c) * W + w]),
+                                  kNegLog2e * bf16_to_f32(p.conv_w[int64_t(c + 1) * W + w]));
     }
     auto bias2 = [&](int ch) {
         const int c = chan(ch);
-        return p.conv_b ? make_float2(bf16_to_f32(p.conv_b[c]), bf16_to_f32(p.conv_b[c + 1]))
+        return p.conv_b ? make_float2(kNegLog2e * bf16_to_f32(p.conv_b[c]),
+                                      kNegLog2e * bf16_to_f32(p.conv_b[c + 1]))
                         : make_float2(0.f, 0.f);
     };
     const int qkp = min(lane, QKP - 1);  // the lane's pair (clamped; idle lanes recompute)
@@ -915,9 +920,13 @@ void prefill_kernel(PrefillParams p)
         issue(k + 1);
         float ss[TPW];
         const bool own = lane < QKP;
+        // u = y sigmoid(-y ln 2) = -log2(e) silu(x) for y = -log2(e) x
+        auto silu_scaled = [](float y) {
+            return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
+        };
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-            xs[i] = make_float2(silu(xs[i].x), silu(xs[i].y));
+            xs[i] = make_float2(silu_scaled(xs[i].x), silu_scaled(xs[i].y));
             ss[i] = own ? fmaf(xs[i].x, xs[i].x, xs[i].y * xs[i].y) : 0.f;
         }
         // wave sums: halves (tokens 0|1 and 2|3 share a register), then rows
@@ -935,7 +944,9 @@ void prefill_kernel(PrefillParams p)
         const float tsum = group_sum<16>(fold_rows(fold_halves(ss[0], ss[1]), fold_halves(ss[2], ss[3])));
         // row j of the sums holds token (0, 2, 1, 3)[j]; lane i < 4 takes token i's
         const int src = 16 * (((lane & 1) << 1) | ((lane >> 1) & 1));
-        const float rx = (ty == 0 ? p.scale : 1.f) * __builtin_amdgcn_rsqf(__shfl(tsum, src, 64) + p.eps);
+        // with s = silu(x) = u / -log2(e): s / sqrt(|s|^2 + eps) = -u / sqrt(|u|^2 + log2(e)^2 eps)
+        const float rx = (ty == 0 ? -p.scale : -1.f) *
+                         __builtin_amdgcn_rsqf(__shfl(tsum, src, 64) + p.eps * (kNegLog2e * kNegLog2e));
         if (own) {
             // the lane's keys 2 lane and 2 lane + 1 sit side by side in a row
             const int kp = key_pos<Sh::X32>(2 * lane);

@@ -34,7 +34,8 @@
 // state's largest entry, against 1e-4 allowed).  A 16x16x32 bf16 MFMA costs
 // 16 cycles, a 16x16x4 fp32 MFMA (the same fp32 product over 4 keys) 32, and
 // an fp32 MFMA stops the other waves' vector issue on its SIMD while it runs,
-// so the chunk's two 16x16 products (T R and D M^T) are split the same way.
+// so the chunk's 16x16 products (T R, D M^T and the state update) are split
+// the same way, each on two 16x16x32 MFMAs.
 //
 // Parallel structure.  A workgroup takes one (sequence, v-head, slice of ISZ
 // value columns); its waves have two roles:

@@ -72,7 +72,7 @@
 // A chunk is prepared in interval c (conv), finished in c + 1 (T, M, decays)
 // and consumed by the state waves in c + 2; one barrier ends each interval,
 // so q^/k^ rows are triple-buffered and T, M and the coefficients double-
-// buffered (about 104 KB of LDS at head size 128: one workgroup per CU).
+// buffered (about 100 KB of LDS at head size 128: one workgroup per CU).
 // The state is plain at every chunk boundary (no running scale), so a run
 // split at a multiple of 16 tokens and resumed from the written-back state
 // gives the same bits as the straight run.

@@ -45,7 +45,7 @@ def draw_case(seed: int, decode: bool):
 
 
 @pytest.mark.parametrize("decode", [False, True])
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_configuration_matches_oracle(seed, decode):
     g, inp, img, what = draw_case(seed, decode)
     log(what)

@@ -963,7 +963,8 @@ void prefill_kernel(PrefillParams p)
                 *reinterpret_cast<uint32_t*>(&dst[1][t0 + i][kp]) = xl[i];
             }
             if (ty == 1) {
-                // k^ columns of the two keys over the wave's 4 tokens (one 8-byte store each)
+                // k^ columns of the two keys over the wave's 4 tokens: per key one 16-byte
+                // store of the 4 hi halves, then the 4 lo halves
                 *reinterpret_cast<uint4*>(&kc[b3][2 * lane][2 * t0]) =
                     make_uint4(halves<false>(xh[0], xh[1]), halves<false>(xh[2], xh[3]),
                                halves<false>(xl[0], xl[1]), halves<false>(xl[2], xl[3]));

@@ -160,15 +160,15 @@ def test_decode_extreme_decays_match_oracle(d):
     log(f"decode extreme decays d={d}: worst state rel err {e_st:.2e}")
 
 
-@pytest.mark.parametrize("W", [2, 3, 4])
-def test_prefill_workgroup_shapes_agree_bit_for_bit(W):
+@pytest.mark.parametrize("W,Hk,Hv", [(2, 4, 8), (3, 4, 8), (4, 4, 8), (4, 4, 4), (3, 2, 6)])
+def test_prefill_workgroup_shapes_agree_bit_for_bit(W, Hk, Hv):
     """Head size 128 runs in 64-column workgroups when a batch's workgroups all
     fit on the GPU at once and in whole-head workgroups otherwise.  The same
     sequences alone (the first shape) and followed by empty sequences that
     push the batch past the GPU's compute units (the second) must give the
     same bits: every value is computed the same way in both; and both
-    match the oracle.  Every conv width."""
-    g = wl.make_geometry(80, Hk=4, Hv=8, dk=128, dv=128, W=W, page_align=128, extra_pad=128)
+    match the oracle.  Every conv width, and 1, 2 or 3 v-heads per k-head."""
+    g = wl.make_geometry(80, Hk=Hk, Hv=Hv, dk=128, dv=128, W=W, page_align=128, extra_pad=128)
     lens = [70, 33, 1, 48]
     inp, img = case(g, 321, lens, [1, 0, 1, 0], bias=True)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -181,10 +181,11 @@ def test_prefill_workgroup_shapes_agree_bit_for_bit(W):
                                       g.num_slots - 4]),
         has_initial_state=np.concatenate([inp.has_initial_state, np.zeros(n_pad, np.uint8)]))
     a = DevicePool(g, [img])
-    log(f"prefill d=128 W={W} in 64-column workgroups ({len(lens)} sequences)")
+    log(f"prefill d=128 W={W} G={Hv // Hk} in 64-column workgroups ({len(lens)} sequences)")
     t_a = run_prefill(a, 0, inp)
     b = DevicePool(g, [img])
-    log(f"prefill d=128 W={W} in whole-head workgroups ({len(lens) + n_pad} sequences, {n_pad} empty)")
+    log(f"prefill d=128 W={W} G={Hv // Hk} in whole-head workgroups ({len(lens) + n_pad} sequences, "
+        f"{n_pad} empty)")
     t_b = run_prefill(b, 0, padded)
     torch.cuda.synchronize()
     assert np.array_equal(u16(t_a["out"]), u16(t_b["out"])), "outputs differ between shapes"

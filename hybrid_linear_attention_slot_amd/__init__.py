@@ -30,6 +30,8 @@ GDN_ESTATE = -8
 GDN_EIO = -9
 GDN_ECORRUPT = -10
 GDN_ENOMEM = -11
+GDN_STEP_DECODE = 1   # gdn_pool_step_support bits
+GDN_STEP_PREFILL = 2
 
 ERROR_NAMES = {GDN_EINVAL: "GDN_EINVAL", GDN_ERANGE: "GDN_ERANGE", GDN_EOVERLAP: "GDN_EOVERLAP",
                GDN_EALIGN: "GDN_EALIGN", GDN_EUNSUPPORTED: "GDN_EUNSUPPORTED",
@@ -113,6 +115,8 @@ def lib() -> C.CDLL:
         L.gdn_pool_destroy.restype = None
         L.gdn_pool_region_bytes.argtypes = [p, C.POINTER(i64), C.POINTER(i64)]
         L.gdn_pool_region_bytes.restype = C.c_int
+        L.gdn_pool_step_support.argtypes = [p]
+        L.gdn_pool_step_support.restype = C.c_int
         L.gdn_pool_describe.argtypes = [p, C.c_char_p, C.c_size_t]
         L.gdn_pool_describe.restype = C.c_int
         L.gdn_restore_slots.argtypes = [p, C.POINTER(gdn_restore_op), i32, p, p]
@@ -247,6 +251,11 @@ def gdn_pool_region_bytes(pool: Pool):
     s, c = C.c_int64(), C.c_int64()
     _check(lib().gdn_pool_region_bytes(pool.handle, C.byref(s), C.byref(c)))
     return s.value, c.value
+
+
+def gdn_pool_step_support(pool: Pool) -> int:
+    """Mask of GDN_STEP_DECODE / GDN_STEP_PREFILL for the pool's geometry."""
+    return _check(lib().gdn_pool_step_support(pool.handle))
 
 
 def gdn_pool_describe(pool: Pool) -> str:

@@ -238,6 +238,21 @@ int gdn_pool_region_bytes(const gdn_pool* pool, int64_t* ssm_bytes, int64_t* con
     return GDN_OK;
 }
 
+int gdn_pool_step_support(const gdn_pool* pool)
+{
+    if (!pool)
+        return fail(GDN_EINVAL, "pool is NULL");
+    const gdn_pool_desc& d = pool->desc;
+    if (d.num_v_heads <= 0)
+        return 0;
+    int mask = 0;
+    if (gdn::decode_supported(d.head_k_dim, d.head_v_dim, d.conv_width))
+        mask |= GDN_STEP_DECODE;
+    if (gdn::prefill_supported(d.head_k_dim, d.head_v_dim, d.conv_width))
+        mask |= GDN_STEP_PREFILL;
+    return mask;
+}
+
 int gdn_pool_describe(const gdn_pool* pool, char* buf, size_t len)
 {
     if (!pool)

@@ -100,14 +100,26 @@ typedef struct {
 /* Validate `desc` and build a pool handle (copies the layer table).
  * Checks: sizes positive, regions inside the page and not overlapping,
  * 16-byte alignment of strides, offsets and layer bases (GDN_EALIGN),
- * C == 2*Hk*dk + Hv*dv, Hv % Hk == 0.  Head dims without a compiled decode /
- * prefill variant are accepted (restore, gather and scatter still work) and
- * those two calls then return GDN_EUNSUPPORTED.  *out is set only on success. */
+ * C == 2*Hk*dk + Hv*dv, Hv % Hk == 0.  A pool describes a memory layout, so
+ * any such geometry is accepted: restore, gather and scatter work on all of
+ * them.  The step kernels cover dk == dv in {16, 32, 64, 128} with conv
+ * widths 2-4 (gdn_pool_step_support says which apply); on other pools
+ * gdn_decode_step and gdn_prefill_varlen return GDN_EUNSUPPORTED.  *out is
+ * set only on success. */
 int gdn_pool_create(const gdn_pool_desc* desc, gdn_pool** out);
 void gdn_pool_destroy(gdn_pool* pool);
 
 /* Bytes of the state region and of the window region of one page. */
 int gdn_pool_region_bytes(const gdn_pool* pool, int64_t* ssm_bytes, int64_t* conv_bytes);
+
+/* Which step kernels exist for the pool's geometry: GDN_STEP_DECODE when
+ * gdn_decode_step can run on it, GDN_STEP_PREFILL when gdn_prefill_varlen
+ * and gdn_prefill_varlen_checkpoint can (0 for a conv-window-only pool or
+ * head dims / conv width without a compiled kernel).  Returns the mask
+ * (>= 0), or GDN_EINVAL for a NULL pool.  Host-only; touches no device. */
+#define GDN_STEP_DECODE 1
+#define GDN_STEP_PREFILL 2
+int gdn_pool_step_support(const gdn_pool* pool);
 
 /* Human-readable layout dump (shapes, strides, offsets, padding, which layers
  * are attention-only), NUL-terminated, truncated to `len`.  Returns the

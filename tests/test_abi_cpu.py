@@ -60,12 +60,27 @@ def test_pool_create_and_describe():
     gdn.gdn_pool_destroy(p)
 
 
+@pytest.mark.parametrize("dk,W,mask", [
+    (128, 4, gdn.GDN_STEP_DECODE | gdn.GDN_STEP_PREFILL),
+    (16, 2, gdn.GDN_STEP_DECODE | gdn.GDN_STEP_PREFILL),
+    (64, 3, gdn.GDN_STEP_DECODE | gdn.GDN_STEP_PREFILL),
+    (48, 4, 0),    # a head size without a compiled kernel
+    (128, 5, 0),   # a conv width without one
+])
+def test_step_support_matches_the_compiled_kernels(dk, W, mask):
+    g = wl.make_geometry(8, Hk=1, Hv=2, dk=dk, dv=dk, W=W, page_align=128)
+    p = pool_for(g)
+    assert gdn.gdn_pool_step_support(p) == mask
+    gdn.gdn_pool_destroy(p)
+
+
 def test_block_stride_example_descriptor():
     # conv-window-only pool of the worked example: 48 bf16 in a 128-byte page
     p = gdn.gdn_pool_create([FAKE], num_slots=4, page_stride_bytes=128, conv_offset_bytes=0,
                             ssm_offset_bytes=0, conv_channels=16, conv_width=4, num_k_heads=0,
                             num_v_heads=0, head_k_dim=0, head_v_dim=0)
     assert gdn.gdn_pool_region_bytes(p) == (0, 96)
+    assert gdn.gdn_pool_step_support(p) == 0  # no recurrent state: copies only
     assert "slot stride 64 elements" in gdn.gdn_pool_describe(p)
 
 

@@ -393,7 +393,8 @@ def bench_ceilings(reps=10):
             "what": "libgdn_ceilings kernels: 2 GiB read-only and write-only streams, and the "
                     "in-place read-modify-write of the 2 MiB state region of the decode "
                     "workload's 256 pages (read + write bytes); 1024-thread workgroups, 128 KiB "
-                    f"each, non-temporal; median of {reps} per-call events"}
+                    "each, non-temporal (the read-modify-write's stores at device scope, "
+                    f"SC1 | NT); median of {reps} per-call events"}
 
 
 def cpu_model() -> str:

@@ -78,6 +78,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // its loads and stores, and the hardware drops accesses past num_records.
 constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer, gfx9-family layout
 constexpr int kNonTemporal = 2;          // cache-policy bit: streamed once
+// State stores are non-temporal at device scope (SC1 | NT).  On the 256-row,
+// 32-head update this ran 5 % faster than NT alone (5.95 against 5.66 TB/s);
+// SC1 or SC0 + SC1 without NT, SC0 + NT and cached stores were all slower,
+// and so were SC1 + NT loads.
+constexpr int kStoreDeviceNT = 16 | kNonTemporal;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(float* ssm, int bytes)
 {
@@ -106,7 +111,7 @@ __device__ __forceinline__ void store_row(const f32x4& t, __amdgpu_buffer_rsrc_t
                                           int h, int m)
 {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t), r,
-                                           voff + (h * DK + RPI * m) * DV * 4, 0, kNonTemporal);
+                                           voff + (h * DK + RPI * m) * DV * 4, 0, kStoreDeviceNT);
 }
 
 // Sum over the lanes l, l + S, l + 2S, ... of a wave (S a power of two).

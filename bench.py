@@ -243,16 +243,19 @@ def bench_restore(steps, warmup):
     payload = g.ssm_region_bytes + g.conv_region_bytes
     nbytes = 2 * hits * int(linear.sum()) * payload
     # gather / scatter of the 64 op rows' pages on every GDN layer (one launch
-    # per layer, 48 launches per timed call)
+    # per layer, 48 launches per timed call).  Every layer has dense rows of its
+    # own (6.6 GB in all): with one shared 137 MB pair the dense side of every
+    # call after the first could be served from the GPU's 256 MB last-level
+    # cache instead of HBM.
     idx = torch.from_numpy(np.ascontiguousarray(ops[:, 0])).cuda()
     n = idx.numel()
-    ssm = torch.empty((n, g.ssm_region_bytes), dtype=torch.uint8, device="cuda")
-    conv = torch.empty((n, g.conv_region_bytes), dtype=torch.uint8, device="cuda")
     layers = [l for l, lin in enumerate(linear) if lin]
-    gather = lambda: [gdn.gdn_gather_states(h, l, idx, n, conv, ssm, stream)  # noqa: E731
-                      for l in layers]
-    scatter = lambda: [gdn.gdn_scatter_states(h, l, idx, n, conv, ssm, stream)  # noqa: E731
-                       for l in layers]
+    ssm = [torch.empty((n, g.ssm_region_bytes), dtype=torch.uint8, device="cuda") for _ in layers]
+    conv = [torch.empty((n, g.conv_region_bytes), dtype=torch.uint8, device="cuda") for _ in layers]
+    gather = lambda: [gdn.gdn_gather_states(h, l, idx, n, conv[i], ssm[i], stream)  # noqa: E731
+                      for i, l in enumerate(layers)]
+    scatter = lambda: [gdn.gdn_scatter_states(h, l, idx, n, conv[i], ssm[i], stream)  # noqa: E731
+                       for i, l in enumerate(layers)]
     gs_bytes = 2 * n * len(layers) * payload
     gs = {}
     for name, fn in (("gather", gather), ("scatter", scatter)):
@@ -262,7 +265,8 @@ def bench_restore(steps, warmup):
                     "frac_of_hbm_peak": round(gs_bytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     gs["bytes"] = gs_bytes
     gs["what"] = f"{n} pages of each of the {len(layers)} GDN layers to dense rows and back " \
-                 "(one launch per layer, median of 5 per-call events over all layers)"
+                 "(one launch per layer, each layer with dense rows of its own; median of 5 " \
+                 "per-call events over all layers)"
     del ssm, conv
     snap = bench_snapshot(h, int(ops[0, 0]), int(ops[1, 0]), int(linear.sum()) * payload)
     del bufs

@@ -259,17 +259,16 @@ __device__ __forceinline__ void zero_units(uint8_t* dst, int64_t n)
 // units are numbered row by row (row r: its state units, then its window
 // units); workgroup w of the grid takes units [U w / G, U (w + 1) / G) and
 // walks the (row, region) pieces they cover.  All indices are wave-uniform.
-// A gather stores into the dense rows non-temporal at device scope (SC1 | NT):
-// about 1 % faster than NT alone over three alternating runs of the 64-page,
-// 48-layer calls.  A scatter's stores into pool pages ran 1-2 % slower that
-// way and stay NT.
+// Stores are non-temporal at device scope (SC1 | NT): over alternating runs of
+// the 64-page calls on 48 layers, each layer with dense rows of its own, a
+// gather ran 1-2 % and a scatter about 1.5 % faster than with NT alone.
 template <bool kGather>
 __global__ __launch_bounds__(kCopyThreads) void rows_balanced_kernel(RowCopyArgs a)
 {
     const int64_t us = a.r.bytes[0] >> 4, uw = a.r.bytes[1] >> 4;
     const int64_t upr = us + uw; // units per row
     const int64_t total = upr * a.n;
-    constexpr int kStorePolicy = kGather ? kDeviceNonTemporal : kNonTemporal;
+    constexpr int kStorePolicy = kDeviceNonTemporal;
     const int64_t end = total * (blockIdx.x + 1) / gridDim.x;
     int64_t u = total * blockIdx.x / gridDim.x;
     while (u < end) {

@@ -186,15 +186,17 @@ __global__ __launch_bounds__(kCopyThreads) void rows_kernel(RowCopyArgs a)
 
 // Copy n consecutive 16-byte units (n < 2^27) through buffer resources of
 // exactly n units: whole 128 KiB blocks with eight loads in flight per lane
-// ahead of the stores, then the remainder as one more block whose rounds past
+// ahead of the stores, then the remainder as one more block whose lanes past
 // the end fall outside the resources (loads return zero, stores are dropped).
+// The buffer range check covers the VGPR offset only, not the SGPR one, so
+// every access of the remainder carries its whole offset in the VGPR; the
+// whole blocks' loads, always in range, take the block offset in an SGPR.
+// Stores always take their whole offset in the VGPR (a 128-bit store with an
+// SGPR offset can read its data registers after a later write to them).
 // The remainder is not guarded round by round: behind a branch per round the
 // compiler waited for every earlier memory operation, stores included, before
 // each store, which serialised the remainder's stores and made each call's
-// last workgroups finish late (gather / scatter 1.5-2 % slower).  Loads take
-// the block offset in an SGPR; stores take their whole offset in the VGPR (a
-// 128-bit store with an SGPR offset can read its data registers after a later
-// write to them).
+// last workgroups finish late (gather / scatter 1.5-2 % slower).
 constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer resource, gfx9-family layout
 constexpr int kNonTemporal = 2;          // cache-policy bit: streamed once
 constexpr int kDeviceNonTemporal = 16 | kNonTemporal; // SC1 | NT
@@ -237,7 +239,7 @@ __device__ __forceinline__ void copy_units(uint8_t* dst, const uint8_t* src, int
     u32x4 v[kCopyUnroll];
 #pragma unroll
     for (int k = 0; k < kCopyUnroll; ++k)
-        v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane, (i + k * kCopyThreads) * 16,
+        v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane + (i + k * kCopyThreads) * 16, 0,
                                                      kNonTemporal);
 #pragma unroll
     for (int k = 0; k < kCopyUnroll; ++k)

@@ -11,6 +11,11 @@ is now one unguarded block whose rounds past the end fall outside the buffer
 resources.  This test compiles the copy kernels and checks that no store of
 the gather / scatter kernels has a wait for all memory operations in its own
 basic block.
+
+The remainder's lanes past the end rely on the buffer range check, which
+covers the VGPR offset of an access but not its SGPR offset; so the
+remainder's loads must carry their whole offset in the VGPR (a zero SGPR
+offset), or lanes past the end would read up to a block beyond the region.
 """
 import os
 import re
@@ -72,3 +77,11 @@ def test_no_store_waits_for_all_memory_operations(copy_asm):
     for name, lines in kernel_lines(copy_asm, "rows_balanced_kernel").items():
         assert sum(l.startswith("buffer_store") for l in lines) >= 16, name
         assert stores_after_full_wait(lines) == [], name
+
+
+def test_remainder_loads_are_range_checked_in_full(copy_asm):
+    # eight loads per lane in the remainder block, each with a zero SGPR offset
+    for name, lines in kernel_lines(copy_asm, "rows_balanced_kernel").items():
+        loads = [l for l in lines if l.startswith("buffer_load")]
+        zero_soffset = [l for l in loads if re.search(r"\], 0 offen", l)]
+        assert len(zero_soffset) >= 8, (name, loads)

@@ -5,7 +5,9 @@ bias and q scale are drawn per case, for the varlen prefill and the decode
 step.  Each case is small; together they cover combinations the fixed cases
 do not.  GDN_RANDOM_SEEDS sets the number of seeds (default 40; a wider sweep,
 e.g. 5440, takes a couple of minutes), and a tenth as many window-first
-layouts run, at least 6."""
+layouts run, at least 6.  The long-sequence cases (GDN_LONG_SEEDS, default 4)
+draw ragged sequences of up to 3000 tokens, so that rounding has many chunks
+to build up over."""
 import os
 
 import numpy as np
@@ -21,6 +23,7 @@ from gpu_util import (DevicePool, check_outputs, check_pages, log, run_decode, r
 pytestmark = pytest.mark.gpu
 
 N_SEEDS = int(os.environ.get("GDN_RANDOM_SEEDS", "40"))
+N_LONG = int(os.environ.get("GDN_LONG_SEEDS", "4"))
 
 
 def draw_case(seed: int, decode: bool):
@@ -144,3 +147,36 @@ def test_window_first_layout_matches_oracle(seed):
         pay[g.conv_off + g.conv_region_bytes:g.ssm_off] = False
         pay[g.ssm_off + g.ssm_region_bytes:] = False
         assert np.array_equal(got[s][~pay], img[s][~pay]), what + ": gap or padding bytes changed"
+
+
+@pytest.mark.parametrize("seed", range(N_LONG))
+def test_random_long_sequences_match_oracle(seed):
+    r = np.random.default_rng(50_000 + seed)
+    d = int(r.choice([32, 64, 128, 128]))
+    Hk = int(r.integers(1, 3))
+    G = int(r.integers(1, 3))
+    W = int(r.integers(2, 5))
+    g = wl.make_geometry(16, Hk=Hk, Hv=Hk * G, dk=d, dv=d, W=W, page_align=128)
+    n = int(r.integers(1, 5))
+    lengths = [int(x) for x in r.integers(1, 3000, size=n)]
+    slots = r.permutation(g.num_slots)[:n].astype(np.int32)
+    warm = (r.random(n) < 0.6).astype(np.uint8)
+    rng = wl.rng_for(60_000 + seed)
+    img = wl.make_pool_image(g, rng, warm_slots=slots[warm == 1], nan_slots=slots[warm == 0],
+                             sigma_s=0.5)
+    long_memory = bool(r.random() < 0.5)
+    inp = wl.step_inputs(g, rng, lengths, slots, warm, bias=bool(r.random() < 0.5),
+                         long_memory=long_memory)
+    inp.scale = float(r.uniform(0.5, 1.5))
+    what = (f"long seed {seed}: d={d} Hk={Hk} G={G} W={W} lengths={lengths} "
+            f"warm={warm.tolist()} long_memory={long_memory}")
+    log(what)
+    dp = DevicePool(g, [img])
+    t = run_prefill(dp, 0, inp)
+    torch.cuda.synchronize()
+    ref = img.copy()
+    o64, _ = oracle.gdn_layer(ref, g, inp.cu_seqlens, inp.state_indices, inp.has_initial_state,
+                              inp.x, inp.conv_w, inp.conv_b, inp.alpha, inp.beta, inp.scale,
+                              inp.eps)
+    check_outputs(u16(t["out"]), o64, what)
+    check_pages(g, dp.host(), ref, slots=[int(x) for x in slots], what=what)

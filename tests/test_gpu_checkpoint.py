@@ -8,9 +8,13 @@ sequence's own page.  Checked against the oracle's prefix runs (small shapes,
 every head size, ragged lengths, requests at token 1, at chunk edges, at the
 end, and ignored ones) and, at the 8-sequence workload's full size, bit for
 bit against a separate GPU prefill of the prefixes.  The call's ordinary
-results must be those of gdn_prefill_varlen.
+results must be those of gdn_prefill_varlen.  Seeded random cases (head size,
+GQA ratio, conv width, lengths, request positions, ignored requests; the
+number of seeds from GDN_CKPT_SEEDS, default 8) cover the combinations the
+fixed ones do not.
 """
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -178,3 +182,65 @@ def test_checkpoint_emission_in_whole_head_workgroups():
         assert np.array_equal(page[0, pad], img[spare[n], pad])
         want[0, pad] = page[0, pad]
         check_pages(sub, page, want, what=f"whole-head checkpoint of sequence {n}")
+
+
+@pytest.mark.parametrize("seed", range(int(os.environ.get("GDN_CKPT_SEEDS", "8"))))
+def test_random_checkpoint_requests_match_oracle_prefix(seed):
+    r = np.random.default_rng(70_000 + seed)
+    d = int(r.choice([16, 32, 64, 128]))
+    Hk = int(r.integers(1, 3))
+    G = int(r.integers(1, 4))
+    W = int(r.integers(2, 5))
+    g = wl.make_geometry(24, Hk=Hk, Hv=Hk * G, dk=d, dv=d, W=W, page_align=128, extra_pad=128)
+    n = int(r.integers(1, 6))
+    lens = [int(x) for x in r.integers(0, 200, size=n)]
+    perm = r.permutation(g.num_slots).astype(np.int32)
+    idx, spare = perm[:n], perm[n:2 * n]
+    hs = (r.random(n) < 0.6).astype(np.uint8)
+    ck_len = np.zeros(n, np.int32)
+    ck_slot = np.full(n, -1, np.int32)
+    valid = []
+    for i in range(n):
+        kind = r.random()
+        if kind < 0.7 and lens[i] > 0:  # a request inside the sequence
+            ck_len[i] = int(r.integers(1, lens[i] + 1))
+            ck_slot[i] = spare[i]
+            valid.append(i)
+        elif kind < 0.85:  # ignored: zero tokens, or past the end
+            ck_len[i] = int(r.choice([0, lens[i] + 1 + int(r.integers(0, 20))]))
+            ck_slot[i] = spare[i]
+        # otherwise no request (slot -1)
+    rng = wl.rng_for(80_000 + seed)
+    img = wl.make_pool_image(g, rng, warm_slots=idx[hs == 1], nan_slots=idx[hs == 0],
+                             sigma_s=0.5)
+    inp = wl.step_inputs(g, rng, lens, idx, hs, bias=bool(r.random() < 0.5),
+                         long_memory=bool(r.random() < 0.3))
+    inp.scale = float(r.uniform(0.5, 1.5))
+    what = (f"checkpoint seed {seed}: d={d} Hk={Hk} G={G} W={W} lens={lens} "
+            f"ck_len={ck_len.tolist()} ck_slot={ck_slot.tolist()} warm={hs.tolist()}")
+    log(what)
+    dp = DevicePool(g, [img])
+    t = step_tensors(inp)
+    rc = gdn.gdn_prefill_varlen_checkpoint(dp.pool, 0, inp.num_seqs, t["cu"], inp.max_seqlen,
+                                           inp.total_tokens, args_of(t, inp), to_dev(ck_slot),
+                                           to_dev(ck_len))
+    assert rc == gdn.GDN_OK
+    torch.cuda.synchronize()
+    got = dp.host()
+    ref = img.copy()
+    o64, _ = oracle.gdn_layer(ref, g, inp.cu_seqlens, inp.state_indices, inp.has_initial_state,
+                              inp.x, inp.conv_w, inp.conv_b, inp.alpha, inp.beta, inp.scale,
+                              inp.eps)
+    if inp.total_tokens:
+        check_outputs(u16(t["out"]), o64, what)
+    for i in valid:
+        ref[ck_slot[i]] = got[ck_slot[i]]  # compared below against the prefix runs
+    check_pages(g, got, ref, slots=[int(x) for x in idx], what=what)
+    sub = dataclasses.replace(g, num_slots=1)
+    pad = slice(g.conv_off + g.conv_region_bytes, g.page_stride)
+    for i in valid:
+        want = oracle_prefix_page(img, inp, i, int(ck_len[i]))
+        page = got[ck_slot[i]][None].copy()
+        assert np.array_equal(page[0, pad], img[ck_slot[i], pad]), what
+        want[0, pad] = page[0, pad]
+        check_pages(sub, page, want, what=f"{what}: checkpoint of sequence {i}")

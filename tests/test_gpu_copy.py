@@ -1,6 +1,9 @@
 """GPU parity of restore / gather / scatter against the oracle: bit-exact,
-padding and unselected pages included (via the C-ABI)."""
+padding and unselected pages included (via the C-ABI).  Seeded random cases
+(GDN_COPY_SEEDS, default 8) draw the page layout, the layer stack, the ops and
+the dense rows' alignment."""
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -243,3 +246,92 @@ def test_restore_gather_scatter_full_hybrid_stack():
     gdn.gdn_pool_destroy(pool)
     del bufs
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("seed", range(int(os.environ.get("GDN_COPY_SEEDS", "8"))))
+def test_random_restore_gather_scatter_match_oracle(seed):
+    r = np.random.default_rng(90_000 + seed)
+    num_slots = int(r.integers(24, 121))
+    if r.random() < 0.25:  # window-only pool, window bytes often not a multiple of 16
+        C, W = 2 * int(r.integers(1, 20)), int(r.integers(2, 5))  # C is even
+        stride = wl.round_up((W - 1) * C * 2, 16) + 16 * int(r.integers(0, 8))
+        g = wl.Geometry(num_slots=num_slots, C=C, W=W, Hk=0, Hv=0, dk=0, dv=0,
+                        page_stride=stride, ssm_off=0, conv_off=0)
+    else:
+        d = int(r.choice([16, 32]))
+        Hk = int(r.integers(1, 3))
+        g = wl.make_geometry(num_slots, Hk=Hk, Hv=Hk * int(r.integers(1, 3)), dk=d, dv=d,
+                             W=int(r.integers(2, 5)), page_align=128,
+                             extra_pad=int(r.choice([0, 16, 128, 4096])))
+    n_layers = int(r.integers(1, 71))
+    linear = r.random(n_layers) >= 0.3
+    imgs = [r.integers(0, 256, (g.num_slots, g.page_stride), dtype=np.uint8) if lin else None
+            for lin in linear]
+    what = (f"copy seed {seed}: slots={num_slots} C={g.C} W={g.W} Hv={g.Hv} d={g.dk} "
+            f"stride={g.page_stride} layers={n_layers} gdn={int(linear.sum())}")
+    log(what)
+    dp = DevicePool(g, imgs)
+
+    # restore: distinct dst slots, src from the other slots (shared ones too), misses,
+    # rows that ask for nothing, prefilled has_initial_state
+    n = int(r.integers(1, min(150, num_slots // 2) + 1))
+    perm = r.permutation(g.num_slots).astype(np.int32)
+    dst, others = perm[:n], perm[n:]
+    src = np.where(r.random(n) < 0.25, -1, r.choice(others, n)).astype(np.int32)
+    req = (r.random(n) < 0.85).astype(np.int32)
+    ops = np.stack([dst, src, req], axis=1).astype(np.int32)
+    hs0 = r.integers(0, 2, n).astype(np.uint8)
+    hs = to_dev(hs0)
+    rc = gdn.gdn_restore_slots(dp.pool, ops.tolist(), hs)
+    torch.cuda.synchronize()
+    ref = [None if im is None else im.copy() for im in imgs]
+    h_ref = hs0.copy()
+    want_rc = oracle.restore(ref, g, ops, h_ref)
+    assert rc == (gdn.GDN_WARN_COLD_FALLBACK if want_rc else gdn.GDN_OK), what
+    assert np.array_equal(hs.cpu().numpy(), h_ref), what
+    for l in range(n_layers):
+        if ref[l] is not None:
+            assert np.array_equal(dp.host(l), ref[l]), f"{what}: restore layer {l}"
+    if not linear.any():
+        return
+
+    # gather then scatter on one GDN layer: out-of-range rows, dense rows at an
+    # offset of 0, 2 or 4 bytes (the element path when not 16-byte aligned)
+    layer = int(r.choice(np.flatnonzero(linear)))
+    m = int(r.integers(1, 40))
+    idx = r.integers(-2, g.num_slots + 2, m).astype(np.int32)
+    ssm_b, conv_b = g.ssm_region_bytes, g.conv_region_bytes
+    off_c = int(r.choice([0, 2]))
+    off_s = int(r.choice([0, 4])) if ssm_b else 0
+    cbuf = torch.full((m * conv_b + 16,), 0x5A, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((m * ssm_b + 16,), 0x5A, dtype=torch.uint8, device="cuda")
+    cd = cbuf[off_c:off_c + m * conv_b]
+    sd = sbuf[off_s:off_s + m * ssm_b] if ssm_b else None
+    gdn.gdn_gather_states(dp.pool, layer, to_dev(idx), m, cd, sd)
+    torch.cuda.synchronize()
+    pool_now = ref[layer]
+    rs, rcd = oracle.gather(pool_now, g, idx)
+    assert np.array_equal(cd.cpu().numpy().reshape(m, conv_b), rcd), f"{what}: gather window"
+    if ssm_b:
+        assert np.array_equal(sd.cpu().numpy().reshape(m, ssm_b), rs), f"{what}: gather state"
+    # the bytes around the dense rows are untouched
+    assert (cbuf[:off_c].cpu().numpy() == 0x5A).all() and \
+        (cbuf[off_c + m * conv_b:].cpu().numpy() == 0x5A).all(), what
+    new_s = r.integers(0, 256, rs.shape, dtype=np.uint8)
+    new_c = r.integers(0, 256, rcd.shape, dtype=np.uint8)
+    cd.copy_(torch.from_numpy(new_c.reshape(-1)).cuda())
+    if ssm_b:
+        sd.copy_(torch.from_numpy(new_s.reshape(-1)).cuda())
+    # scatter needs distinct in-range rows; repeated slots keep the last writer
+    # undefined, so the scatter uses the first occurrence of each slot only
+    keep = np.zeros(m, bool)
+    seen = set()
+    for i, s_ in enumerate(idx.tolist()):
+        if s_ not in seen:
+            keep[i] = True
+            seen.add(s_)
+    sidx = np.where(keep, idx, -1).astype(np.int32)
+    gdn.gdn_scatter_states(dp.pool, layer, to_dev(sidx), m, cd, sd)
+    torch.cuda.synchronize()
+    oracle.scatter(pool_now, g, sidx, new_s, new_c)
+    assert np.array_equal(dp.host(layer), pool_now), f"{what}: scatter"

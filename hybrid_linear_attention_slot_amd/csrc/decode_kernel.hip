@@ -12,9 +12,11 @@
 // Cache 内部机制" §0: the slot is overwritten in place every step).
 //
 // Design (HBM-bound; MFMA is of no use for rank-1 updates and mat-vecs):
-//   - one workgroup per (row, k-head g).  It owns the q and k conv channels
-//     of g and the v channels of the Hv/Hk v-heads that read g, so no two
-//     workgroups touch the same window channels, and q/k are computed once.
+//   - one group of waves per (row, k-head g), one or more such groups per
+//     workgroup (several for small heads, below).  A group owns the q and k
+//     conv channels of g and the v channels of the Hv/Hk v-heads that read g,
+//     so no two groups touch the same window channels, and q/k are computed
+//     once.
 //   - each v-head's dk x dv fp32 state tile is streamed once from HBM into
 //     registers and once back.  The tile is stored key-major ([dk][dv], value
 //     index contiguous).  Wave w owns the key rows [w KPW, (w+1) KPW) of every
@@ -202,12 +204,11 @@ __device__ __forceinline__ void finish_conv_pair(const ConvPairIn<W>& in, uint32
 // [2 heads][u | o][NW waves][DV].
 template <int DK, int DV, int W, bool WARM>
 __device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, float* red, int row,
-                                             int g, uint8_t* page)
+                                             int g, uint8_t* page, int tid)
 {
     using Sh = DecodeShape<DK, DV>;
     constexpr int JPL = Sh::JPL, RPI = Sh::RPI, LPR = Sh::LPR, NW = Sh::NW;
     const int G = p.Hv / p.Hk;
-    const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int c4 = lane % LPR;                     // float4 column of the lane
@@ -346,31 +347,36 @@ __device__ __forceinline__ void decode_group(const DecodeParams& p, float* ys, f
     }
 }
 
-template <int DK, int DV, int W>
-__global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
+template <int DK, int DV, int W, int KPG>
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NT * KPG)) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeParams p)
 {
     using Sh = DecodeShape<DK, DV>;
-    extern __shared__ float ys[]; // conv outputs: q (DK) | k (DK) | v (G*DV); partial sums
-    const int row = blockIdx.x / p.Hk;
-    const int g = blockIdx.x - row * p.Hk;
+    // per k-head: conv outputs q (DK) | k (DK) | v (G*DV), then partial sums
+    extern __shared__ float lds[];
+    const int G = p.Hv / p.Hk;
+    const int per_row = p.Hk / KPG; // workgroups per row
+    const int row = blockIdx.x / per_row;
+    const int g0 = (blockIdx.x - row * per_row) * KPG;
     const int slot = p.state_indices[row];
     if (slot < 0 || slot >= p.num_slots) { // padding row: zero output, no state I/O
-        const int G = p.Hv / p.Hk;
-        uint16_t* out_row = p.out + (int64_t(row) * p.Hv + g * G) * DV;
-        for (int e = threadIdx.x; e < G * DV; e += Sh::NT)
+        uint16_t* out_row = p.out + (int64_t(row) * p.Hv + g0 * G) * DV;
+        for (int e = threadIdx.x; e < KPG * G * DV; e += KPG * Sh::NT)
             out_row[e] = 0;
         return;
     }
+    const int sub = KPG > 1 ? int(threadIdx.x) / Sh::NT : 0;
+    float* ys = lds + sub * (2 * DK + G * DV + 4 * Sh::NW * DV);
     uint8_t* page = p.layer + int64_t(slot) * p.page_stride;
-    float* red = ys + 2 * DK + (p.Hv / p.Hk) * DV;
+    float* red = ys + 2 * DK + G * DV;
+    const int tid = KPG > 1 ? int(threadIdx.x) % Sh::NT : int(threadIdx.x);
     if (p.hs[row] != 0)
-        decode_group<DK, DV, W, true>(p, ys, red, row, g, page);
+        decode_group<DK, DV, W, true>(p, ys, red, row, g0 + sub, page, tid);
     else
-        decode_group<DK, DV, W, false>(p, ys, red, row, g, page);
+        decode_group<DK, DV, W, false>(p, ys, red, row, g0 + sub, page, tid);
 }
 
-template <int DK, int DV, int W>
+template <int DK, int DV, int W, int KPG>
 int launch_decode_t(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn_step_args* a,
                     hipStream_t stream)
 {
@@ -396,25 +402,44 @@ int launch_decode_t(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn
     p.scale = a->scale;
     p.eps = a->l2_eps;
     const int G = d.num_v_heads / d.num_k_heads;
-    const size_t lds = sizeof(float) * size_t(2 * DK + G * DV + 2 * 2 * Sh::NW * DV);
-    const int64_t blocks = int64_t(rows) * d.num_k_heads;
+    const size_t lds = sizeof(float) * size_t(KPG) * size_t(2 * DK + G * DV + 2 * 2 * Sh::NW * DV);
+    const int64_t blocks = int64_t(rows) * (d.num_k_heads / KPG);
     if (blocks > INT32_MAX)
         return fail(GDN_ERANGE, "decode grid too large");
-    hipLaunchKernelGGL((decode_kernel<DK, DV, W>), dim3(uint32_t(blocks)), dim3(Sh::NT), lds, stream,
-                       p);
+    hipLaunchKernelGGL((decode_kernel<DK, DV, W, KPG>), dim3(uint32_t(blocks)), dim3(Sh::NT * KPG),
+                       lds, stream, p);
     return check_launch("decode");
+}
+
+// k-heads per workgroup.  A small head moves few bytes per k-head, and
+// workgroups of 256 threads or fewer with 32 KiB or less each kept the HBM
+// short of work; 512-thread workgroups ran fastest (512 MiB of state per step:
+// head size 64 5.70 against 5.38 TB/s with one k-head per workgroup, 32 5.86
+// against 5.40, 16 4.20 against 4.0; twice as many k-heads per workgroup was
+// slower at every size).  A pool whose k-head count the choice does not
+// divide takes one k-head per workgroup.
+constexpr int kpg_for(int dk) { return dk == 64 ? 2 : dk == 32 ? 8 : dk == 16 ? 8 : 1; }
+
+template <int DK, int KPG>
+int dispatch_kpg(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn_step_args* a,
+                 hipStream_t stream)
+{
+    switch (pool->desc.conv_width) {
+    case 2: return launch_decode_t<DK, DK, 2, KPG>(pool, layer, rows, a, stream);
+    case 3: return launch_decode_t<DK, DK, 3, KPG>(pool, layer, rows, a, stream);
+    case 4: return launch_decode_t<DK, DK, 4, KPG>(pool, layer, rows, a, stream);
+    default: return fail(GDN_EUNSUPPORTED, "decode: conv width %d", pool->desc.conv_width);
+    }
 }
 
 template <int DK>
 int dispatch_w(const gdn_pool* pool, int32_t layer, int32_t rows, const gdn_step_args* a,
                hipStream_t stream)
 {
-    switch (pool->desc.conv_width) {
-    case 2: return launch_decode_t<DK, DK, 2>(pool, layer, rows, a, stream);
-    case 3: return launch_decode_t<DK, DK, 3>(pool, layer, rows, a, stream);
-    case 4: return launch_decode_t<DK, DK, 4>(pool, layer, rows, a, stream);
-    default: return fail(GDN_EUNSUPPORTED, "decode: conv width %d", pool->desc.conv_width);
-    }
+    constexpr int K = kpg_for(DK);
+    if (K > 1 && pool->desc.num_k_heads % K == 0)
+        return dispatch_kpg<DK, K>(pool, layer, rows, a, stream);
+    return dispatch_kpg<DK, 1>(pool, layer, rows, a, stream);
 }
 
 } // namespace

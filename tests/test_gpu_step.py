@@ -81,6 +81,22 @@ def test_wider_gqa_groups_match_oracle(Hk, Hv, d):
     run_and_check(g, inp, img, "prefill", f"prefill G={Hv // Hk} d={d}")
 
 
+@pytest.mark.parametrize("Hk,Hv,d", [(2, 4, 64), (4, 4, 64), (8, 16, 32), (16, 16, 32),
+                                     (24, 48, 32), (8, 24, 16), (16, 32, 16)])
+def test_decode_grouped_workgroups_match_oracle(Hk, Hv, d):
+    """Small heads run several k-heads per workgroup (2 at head size 64, 8 at
+    32 and 16) when the k-head count allows: each group of waves has its own
+    window channels, tiles and partial sums, and a padding row zeroes the
+    outputs of all the workgroup's k-heads."""
+    g = wl.make_geometry(40, Hk=Hk, Hv=Hv, dk=d, dv=d, W=4, page_align=128, extra_pad=128)
+    rng = wl.rng_for(800 + Hk + d)
+    slots = rng.permutation(g.num_slots)[:9].astype(np.int32)
+    slots[3], slots[7] = -1, g.num_slots  # padding rows
+    inp, img = case(g, 801 + Hk + d, [1] * 9, [1, 0, 1, 1, 1, 0, 1, 1, 0], slots=slots,
+                    bias=True, scale=0.9)
+    run_and_check(g, inp, img, "decode", f"decode grouped Hk={Hk} G={Hv // Hk} d={d}")
+
+
 def extreme_decays(rng, T, Hv):
     """Decays that drive the running product of a chunk below 2^-40: runs of
     0.02 (below it after 8 tokens), exact zeros, 1e-30 and a subnormal, exact

@@ -7,7 +7,9 @@ do not.  GDN_RANDOM_SEEDS sets the number of seeds (default 40; a wider sweep,
 e.g. 5440, takes a couple of minutes), and a tenth as many window-first
 layouts run, at least 6.  The long-sequence cases (GDN_LONG_SEEDS, default 4)
 draw ragged sequences of up to 3000 tokens, so that rounding has many chunks
-to build up over."""
+to build up over.  The grouped decode cases (GDN_GROUPED_SEEDS, default 8)
+draw small heads with 2-16 k-heads, the shapes whose decode runs several
+k-heads per workgroup."""
 import os
 
 import numpy as np
@@ -24,6 +26,7 @@ pytestmark = pytest.mark.gpu
 
 N_SEEDS = int(os.environ.get("GDN_RANDOM_SEEDS", "40"))
 N_LONG = int(os.environ.get("GDN_LONG_SEEDS", "4"))
+N_GROUPED = int(os.environ.get("GDN_GROUPED_SEEDS", "8"))
 
 
 def draw_case(seed: int, decode: bool):
@@ -180,3 +183,37 @@ def test_random_long_sequences_match_oracle(seed):
                               inp.eps)
     check_outputs(u16(t["out"]), o64, what)
     check_pages(g, dp.host(), ref, slots=[int(x) for x in slots], what=what)
+
+
+@pytest.mark.parametrize("seed", range(N_GROUPED))
+def test_random_grouped_decode_matches_oracle(seed):
+    r = np.random.default_rng(123_000 + seed)
+    d = int(r.choice([16, 32, 64]))
+    Hk = int(r.choice([2, 4, 8, 16]))
+    G = int(r.integers(1, 5))
+    W = int(r.integers(2, 5))
+    g = wl.make_geometry(48, Hk=Hk, Hv=Hk * G, dk=d, dv=d, W=W, page_align=128,
+                         extra_pad=int(r.choice([0, 128])))
+    n = int(r.integers(1, 12))
+    slots = r.permutation(g.num_slots)[:n].astype(np.int32)
+    if n > 1 and r.random() < 0.5:
+        slots[int(r.integers(0, n))] = int(r.choice([-1, g.num_slots]))  # a padding row
+    warm = (r.random(n) < 0.7).astype(np.uint8)
+    rng = wl.rng_for(124_000 + seed)
+    valid = (slots >= 0) & (slots < g.num_slots)
+    img = wl.make_pool_image(g, rng, warm_slots=slots[valid & (warm == 1)],
+                             nan_slots=slots[valid & (warm == 0)], sigma_s=0.5)
+    inp = wl.step_inputs(g, rng, [1] * n, slots, warm, bias=bool(r.random() < 0.5),
+                         long_memory=bool(r.random() < 0.3))
+    inp.scale = float(r.uniform(0.5, 1.5))
+    what = f"grouped seed {seed}: d={d} Hk={Hk} G={G} W={W} slots={slots.tolist()}"
+    log(what)
+    dp = DevicePool(g, [img])
+    t = run_decode(dp, 0, inp)
+    torch.cuda.synchronize()
+    ref = img.copy()
+    o64, _ = oracle.gdn_layer(ref, g, inp.cu_seqlens, inp.state_indices, inp.has_initial_state,
+                              inp.x, inp.conv_w, inp.conv_b, inp.alpha, inp.beta, inp.scale,
+                              inp.eps)
+    check_outputs(u16(t["out"]), o64, what)
+    check_pages(g, dp.host(), ref, slots=[int(x) for x in slots[valid]], what=what)

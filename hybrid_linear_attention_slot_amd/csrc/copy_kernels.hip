@@ -188,9 +188,10 @@ __global__ __launch_bounds__(kCopyThreads) void rows_kernel(RowCopyArgs a)
 // exactly n units: whole 128 KiB blocks with eight loads in flight per lane
 // ahead of the stores, then the remainder as one more block whose lanes past
 // the end fall outside the resources (loads return zero, stores are dropped).
-// The buffer range check covers the VGPR offset only, not the SGPR one, so
-// every access of the remainder carries its whole offset in the VGPR; the
-// whole blocks' loads, always in range, take the block offset in an SGPR.
+// The raw buffer intrinsics leave the SGPR offset out of the range check (it
+// covers the VGPR offset), so every access of the remainder carries its whole
+// offset in the VGPR; the whole blocks' loads, always in range, take the
+// block offset in an SGPR.
 // Stores always take their whole offset in the VGPR (a 128-bit store with an
 // SGPR offset can read its data registers after a later write to them).
 // The remainder is not guarded round by round: behind a branch per round the

@@ -13,7 +13,8 @@ the gather / scatter kernels has a wait for all memory operations in its own
 basic block.
 
 The remainder's lanes past the end rely on the buffer range check, which
-covers the VGPR offset of an access but not its SGPR offset; so the
+for the raw buffer intrinsics covers the VGPR offset of an access but not its
+SGPR offset; so the
 remainder's loads must carry their whole offset in the VGPR (a zero SGPR
 offset), or lanes past the end would read up to a block beyond the region.
 """

@@ -9,7 +9,10 @@ layouts run, at least 6.  The long-sequence cases (GDN_LONG_SEEDS, default 4)
 draw ragged sequences of up to 3000 tokens, so that rounding has many chunks
 to build up over.  The grouped decode cases (GDN_GROUPED_SEEDS, default 8)
 draw small heads with 2-16 k-heads, the shapes whose decode runs several
-k-heads per workgroup."""
+k-heads per workgroup.  The chained cases (GDN_CHAIN_SEEDS, default 8) run a
+prefill and then several decode steps on the same slots, so that each kernel
+reads the state and window the other wrote."""
+import dataclasses
 import os
 
 import numpy as np
@@ -27,6 +30,7 @@ pytestmark = pytest.mark.gpu
 N_SEEDS = int(os.environ.get("GDN_RANDOM_SEEDS", "40"))
 N_LONG = int(os.environ.get("GDN_LONG_SEEDS", "4"))
 N_GROUPED = int(os.environ.get("GDN_GROUPED_SEEDS", "8"))
+N_CHAIN = int(os.environ.get("GDN_CHAIN_SEEDS", "8"))
 
 
 def draw_case(seed: int, decode: bool):
@@ -217,3 +221,52 @@ def test_random_grouped_decode_matches_oracle(seed):
                               inp.eps)
     check_outputs(u16(t["out"]), o64, what)
     check_pages(g, dp.host(), ref, slots=[int(x) for x in slots[valid]], what=what)
+
+
+@pytest.mark.parametrize("seed", range(N_CHAIN))
+def test_random_prefill_then_decode_steps_match_oracle(seed):
+    r = np.random.default_rng(140_000 + seed)
+    d = int(r.choice([16, 32, 64, 128]))
+    Hk = int(r.choice([1, 2, 4, 8]))
+    G = int(r.integers(1, 4))
+    W = int(r.integers(2, 5))
+    g = wl.make_geometry(24, Hk=Hk, Hv=Hk * G, dk=d, dv=d, W=W, page_align=128,
+                         extra_pad=int(r.choice([0, 128])))
+    n = int(r.integers(1, 6))
+    slots = r.permutation(g.num_slots)[:n].astype(np.int32)
+    warm = (r.random(n) < 0.5).astype(np.uint8)
+    lens = [int(x) for x in r.integers(0, 80, size=n)]
+    rng = wl.rng_for(141_000 + seed)
+    img = wl.make_pool_image(g, rng, warm_slots=slots[warm == 1], nan_slots=slots[warm == 0],
+                             sigma_s=0.5)
+    long_memory = bool(r.random() < 0.5)
+    pre = wl.step_inputs(g, rng, lens, slots, warm, bias=bool(r.random() < 0.5),
+                         long_memory=long_memory)
+    pre.scale = float(r.uniform(0.5, 1.5))
+    what = (f"chain seed {seed}: d={d} Hk={Hk} G={G} W={W} lens={lens} warm={warm.tolist()}")
+    log(what)
+    dp = DevicePool(g, [img])
+    ref = img.copy()
+    if pre.total_tokens:
+        t = run_prefill(dp, 0, pre)
+        torch.cuda.synchronize()
+        o64, _ = oracle.gdn_layer(ref, g, pre.cu_seqlens, pre.state_indices,
+                                  pre.has_initial_state, pre.x, pre.conv_w, pre.conv_b,
+                                  pre.alpha, pre.beta, pre.scale, pre.eps)
+        check_outputs(u16(t["out"]), o64, f"{what}: prefill")
+    # a row whose prefill was empty keeps its own start state for the decode steps
+    hs = np.where(np.asarray(lens) > 0, 1, warm).astype(np.uint8)
+    for k in range(int(r.integers(1, 6))):
+        x = wl.draw_x(rng, n, g.C)
+        alpha, beta = wl.draw_gates(rng, n, g.Hv, long_memory)
+        step = dataclasses.replace(pre, x=x, alpha=alpha, beta=beta,
+                                   cu_seqlens=np.arange(n + 1, dtype=np.int32),
+                                   has_initial_state=hs.copy())
+        t = run_decode(dp, 0, step)
+        torch.cuda.synchronize()
+        o64, _ = oracle.gdn_layer(ref, g, step.cu_seqlens, step.state_indices,
+                                  step.has_initial_state, step.x, step.conv_w, step.conv_b,
+                                  step.alpha, step.beta, step.scale, step.eps)
+        check_outputs(u16(t["out"]), o64, f"{what}: decode step {k}")
+        hs[:] = 1
+    check_pages(g, dp.host(), ref, slots=[int(x) for x in slots], what=what)

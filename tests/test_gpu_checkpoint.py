@@ -11,7 +11,8 @@ bit against a separate GPU prefill of the prefixes.  The call's ordinary
 results must be those of gdn_prefill_varlen.  Seeded random cases (head size,
 GQA ratio, conv width, lengths, request positions, ignored requests; the
 number of seeds from GDN_CKPT_SEEDS, default 8) cover the combinations the
-fixed ones do not.
+fixed ones do not, and so do random cycles of checkpoint, restore into a fresh
+slot and continuation, checked against the oracle's straight run.
 """
 import dataclasses
 import os
@@ -244,3 +245,72 @@ def test_random_checkpoint_requests_match_oracle_prefix(seed):
         assert np.array_equal(page[0, pad], img[ck_slot[i], pad]), what
         want[0, pad] = page[0, pad]
         check_pages(sub, page, want, what=f"{what}: checkpoint of sequence {i}")
+
+
+@pytest.mark.parametrize("seed", range(int(os.environ.get("GDN_CKPT_SEEDS", "8"))))
+def test_random_checkpoint_restore_continue_matches_oracle(seed):
+    """The prefix-cache cycle on random shapes: a prefill emits each sequence's
+    state after its first c tokens into a checkpoint page, the restore copies
+    the checkpoint into a fresh slot, and a second prefill continues the last
+    L - c tokens there.  The continuation's outputs and final pages must be
+    those of the oracle's straight run over all L tokens."""
+    r = np.random.default_rng(150_000 + seed)
+    d = int(r.choice([16, 32, 64, 128]))
+    Hk = int(r.integers(1, 3))
+    G = int(r.integers(1, 3))
+    W = int(r.integers(2, 5))
+    g = wl.make_geometry(32, Hk=Hk, Hv=Hk * G, dk=d, dv=d, W=W, page_align=128, extra_pad=128)
+    n = int(r.integers(1, 5))
+    lens = [int(x) for x in r.integers(2, 160, size=n)]
+    cks = [int(r.integers(1, L)) for L in lens]  # 1 <= c < L
+    perm = r.permutation(g.num_slots).astype(np.int32)
+    idx, ck_slots, fresh = perm[:n], perm[n:2 * n], perm[2 * n:3 * n]
+    hs = (r.random(n) < 0.5).astype(np.uint8)
+    rng = wl.rng_for(151_000 + seed)
+    img = wl.make_pool_image(g, rng, warm_slots=idx[hs == 1], nan_slots=idx[hs == 0],
+                             sigma_s=0.5)
+    inp = wl.step_inputs(g, rng, lens, idx, hs, bias=bool(r.random() < 0.5),
+                         long_memory=bool(r.random() < 0.5))
+    inp.scale = float(r.uniform(0.5, 1.5))
+    what = f"cycle seed {seed}: d={d} Hk={Hk} G={G} W={W} lens={lens} cks={cks} warm={hs.tolist()}"
+    log(what)
+    # the oracle's straight run over all L tokens of every sequence
+    ref = img.copy()
+    o64, _ = oracle.gdn_layer(ref, g, inp.cu_seqlens, inp.state_indices, inp.has_initial_state,
+                              inp.x, inp.conv_w, inp.conv_b, inp.alpha, inp.beta, inp.scale,
+                              inp.eps)
+    # 1. prefill of every sequence with its checkpoint after c tokens
+    dp = DevicePool(g, [img])
+    t = step_tensors(inp)
+    assert gdn.gdn_prefill_varlen_checkpoint(
+        dp.pool, 0, inp.num_seqs, t["cu"], inp.max_seqlen, inp.total_tokens, args_of(t, inp),
+        to_dev(ck_slots), to_dev(np.array(cks, np.int32))) == gdn.GDN_OK
+    # 2. restore each checkpoint into a fresh slot
+    ops = np.stack([fresh, ck_slots, np.ones(n, np.int32)], axis=1).astype(np.int32)
+    hs2 = to_dev(np.zeros(n, np.uint8))
+    assert gdn.gdn_restore_slots(dp.pool, ops.tolist(), hs2) == gdn.GDN_OK
+    torch.cuda.synchronize()
+    assert hs2.cpu().numpy().tolist() == [1] * n
+    # 3. the last L - c tokens of each sequence, continued on the fresh slot
+    cu = inp.cu_seqlens
+    rows = np.concatenate([np.arange(cu[i] + cks[i], cu[i + 1]) for i in range(n)])
+    rest = [L - c for L, c in zip(lens, cks)]
+    cont = dataclasses.replace(inp, x=inp.x[rows], alpha=inp.alpha[rows], beta=inp.beta[rows],
+                               state_indices=fresh.copy(), has_initial_state=np.ones(n, np.uint8),
+                               cu_seqlens=np.concatenate([[0], np.cumsum(rest)]).astype(np.int32))
+    t2 = step_tensors(cont)
+    rc = gdn.gdn_prefill_varlen(dp.pool, 0, cont.num_seqs, t2["cu"], cont.max_seqlen,
+                                cont.total_tokens, args_of(t2, cont))
+    assert rc == gdn.GDN_OK
+    torch.cuda.synchronize()
+    check_outputs(u16(t2["out"]), o64[rows], f"{what}: continued outputs")
+    got = dp.host()
+    # the fresh slots now hold what the straight run left in the sequences' own slots
+    sub = dataclasses.replace(g, num_slots=1)
+    pad = slice(g.conv_off + g.conv_region_bytes, g.page_stride)
+    for i in range(n):
+        page = got[fresh[i]][None].copy()
+        want = ref[idx[i]][None].copy()
+        want[0, pad] = page[0, pad]
+        assert np.array_equal(page[0, pad], img[fresh[i], pad]), what
+        check_pages(sub, page, want, what=f"{what}: continued page of sequence {i}")

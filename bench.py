@@ -367,6 +367,7 @@ def bench_ceilings(reps=10):
     lib.gdnc_read.argtypes = [p, i64, p, p]
     lib.gdnc_write.argtypes = [p, i64, u32, p]
     lib.gdnc_rmw.argtypes = [p, i64, p, i32, i64, p]
+    lib.gdnc_copy.argtypes = [p, p, i64, p]
     st = torch.cuda.current_stream()
     sp = st.cuda_stream
     n = 2 << 30
@@ -380,6 +381,8 @@ def bench_ceilings(reps=10):
 
     rd = run(lambda: lib.gdnc_read(buf.data_ptr(), n, sink.data_ptr(), sp))
     wr = run(lambda: lib.gdnc_write(buf.data_ptr(), n, 7, sp))
+    half = n // 2  # 1 GiB into the other 1 GiB
+    cp = run(lambda: lib.gdnc_copy(buf.data_ptr(), buf.data_ptr() + half, half, sp))
     del buf, sink
     inp, _ = wl.decode_workload(seed=0)
     g = inp.geom
@@ -394,11 +397,13 @@ def bench_ceilings(reps=10):
     return {"read_gb_per_s": round(n / (rd * 1e-3) / 1e9, 1),
             "write_gb_per_s": round(n / (wr * 1e-3) / 1e9, 1),
             "rmw_gb_per_s": round(nb / (rmw * 1e-3) / 1e9, 1),
-            "what": "libgdn_ceilings kernels: 2 GiB read-only and write-only streams, and the "
-                    "in-place read-modify-write of the 2 MiB state region of the decode "
-                    "workload's 256 pages (read + write bytes); 1024-thread workgroups, 128 KiB "
-                    "each, non-temporal (the read-modify-write's stores at device scope, "
-                    f"SC1 | NT); median of {reps} per-call events"}
+            "copy_gb_per_s": round(2 * half / (cp * 1e-3) / 1e9, 1),
+            "what": "libgdn_ceilings kernels: 2 GiB read-only and write-only streams, a copy "
+                    "of 1 GiB into another (read + write bytes), and the in-place "
+                    "read-modify-write of the 2 MiB state region of the decode workload's 256 "
+                    "pages (read + write bytes); 1024-thread workgroups, 128 KiB each, "
+                    "non-temporal (the read-modify-write's stores at device scope, SC1 | NT); "
+                    f"median of {reps} per-call events"}
 
 
 def cpu_model() -> str:
@@ -644,6 +649,11 @@ def main():
     line["copy_baseline"] = bench_copy()
     ceil = bench_ceilings()
     ceil["decode_frac_of_rmw"] = round(gbs / ceil["rmw_gb_per_s"], 4)
+    if restore is not None:
+        restore["frac_of_copy_ceiling"] = round(restore["gb_per_s"] / ceil["copy_gb_per_s"], 4)
+        for k in ("gather", "scatter"):
+            gsk = restore["gather_scatter"][k]
+            gsk["frac_of_copy_ceiling"] = round(gsk["gb_per_s"] / ceil["copy_gb_per_s"], 4)
     line["hbm_ceilings"] = ceil
     line["slot_manager"] = bench_slot_manager()
     if not a.no_cpu_baseline:

@@ -10,11 +10,16 @@
 //   rmw   -- in place read-modify-write of the state regions of scattered
 //            pages (the decode step's pattern: each row's 2 MiB of state is
 //            read and written back in its own page), one workgroup per 128 KiB
-//            of a region, all eight loads of a lane before its stores.
+//            of a region, all eight loads of a lane before its stores;
+//   copy  -- one buffer into another of the same size (the restore's and the
+//            gather's / scatter's pattern without the page walk), one
+//            workgroup per 128 KiB, all eight loads of a lane before its
+//            stores.
 // Each uses the cache policy that moved its pattern fastest: NT loads and
 // stores for the streams, NT loads and device-scope NT stores (SC1 | NT) for
 // the read-modify-write (6.13 against 5.97 TB/s with NT stores; the write
-// stream ran 2-3 % slower with SC1 | NT).
+// stream ran 2-3 % slower with SC1 | NT, and the copy 1-2 % slower: it
+// keeps NT stores).
 // Built as its own library (libgdn_ceilings.so); the benchmark calls it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -86,6 +91,25 @@ __global__ __launch_bounds__(kThreads) void rmw_kernel(uint8_t* __restrict__ bas
     }
 }
 
+__global__ __launch_bounds__(kThreads) void copy_kernel(const uint8_t* __restrict__ src,
+                                                        uint8_t* __restrict__ dst)
+{
+    const int64_t at = int64_t(blockIdx.x) * kChunkBytes;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(src) + at, short(0), int(kChunkBytes), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rd =
+        __builtin_amdgcn_make_buffer_rsrc(dst + at, short(0), int(kChunkBytes), kBufferWord3);
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k)
+        v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int(threadIdx.x) + k * kThreads) * 16, 0,
+                                                     kNonTemporal);
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(v[k], rd, (int(threadIdx.x) + k * kThreads) * 16, 0,
+                                               kNonTemporal);
+}
+
 int launched() { return hipGetLastError() == hipSuccess ? 0 : -1; }
 
 } // namespace
@@ -111,6 +135,17 @@ int gdnc_write(void* dst, int64_t bytes, uint32_t value, hipStream_t stream)
         return -1;
     hipLaunchKernelGGL(write_kernel, dim3(uint32_t(bytes / kChunkBytes)), dim3(kThreads), 0,
                        stream, static_cast<u32x4*>(dst), value);
+    return launched();
+}
+
+// Copies `bytes` (a positive multiple of 128 KiB) of `src` into `dst`; the
+// two must not overlap.
+int gdnc_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream)
+{
+    if (!src || !dst || bytes <= 0 || bytes % kChunkBytes != 0 || bytes / kChunkBytes > INT32_MAX)
+        return -1;
+    hipLaunchKernelGGL(copy_kernel, dim3(uint32_t(bytes / kChunkBytes)), dim3(kThreads), 0, stream,
+                       static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst));
     return launched();
 }
 
